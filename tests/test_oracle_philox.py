@@ -1,0 +1,76 @@
+"""Pin the oracle's Philox4x32-10 to an independent implementation (CPU only).
+
+PyTorch ships a header-only Philox4x32-10 engine (ATen/core/PhiloxRNGEngine.h)
+whose key is (seed lo, seed hi) and whose counter is (offset lo, offset hi,
+subsequence lo, subsequence hi); successive calls return words 0..3.  The test
+compiles a tiny program against that header with g++ and compares outputs;
+nothing is stored.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from oracle.philox import philox4x32_10, split64, uniform_words
+
+KAT_SRC = r"""
+#include <ATen/core/PhiloxRNGEngine.h>
+#include <cstdio>
+#include <cstdlib>
+int main(int argc, char** argv) {
+  for (int a = 1; a + 2 < argc; a += 3) {
+    unsigned long long seed = strtoull(argv[a], 0, 0), sub = strtoull(argv[a+1], 0, 0), off = strtoull(argv[a+2], 0, 0);
+    at::Philox4_32 eng(seed, sub, off);
+    for (int i = 0; i < 4; i++) printf("%u\n", (unsigned)eng());
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def torch_philox():
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    from torch.utils.cpp_extension import include_paths
+    inc = [p for p in include_paths() if os.path.exists(os.path.join(p, "ATen/core/PhiloxRNGEngine.h"))]
+    if not inc:
+        pytest.skip("torch Philox header not found")
+    d = tempfile.mkdtemp()
+    src, exe = os.path.join(d, "kat.cpp"), os.path.join(d, "kat")
+    with open(src, "w") as f:
+        f.write(KAT_SRC)
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-I" + inc[0], src, "-o", exe])
+
+    def run(triples):
+        args = [exe] + [str(int(v)) for t in triples for v in t]
+        out = subprocess.check_output(args).decode().split()
+        return np.array([int(v) for v in out], dtype=np.uint64).reshape(-1, 4)
+    yield run
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_philox_matches_torch_header(torch_philox):
+    rng = np.random.default_rng(0)
+    triples = [(0, 0, 0), (1, 0, 0), (2 ** 64 - 1, 2, 2 ** 40 + 3)]
+    triples += [(int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 3)), int(rng.integers(0, 2 ** 50)))
+                for _ in range(40)]
+    ref = torch_philox(triples)
+    for (seed, sub, off), want in zip(triples, ref):
+        k0, k1 = split64(np.uint64(seed))
+        o0, o1 = split64(np.uint64(off))
+        s0, s1 = split64(np.uint64(sub))
+        got = np.array([int(w) for w in philox4x32_10(o0, o1, s0, s1, k0, k1)], dtype=np.uint64)
+        assert np.array_equal(got, want), (seed, sub, off)
+
+
+def test_uniform_words_index_layout(torch_philox):
+    # element i uses word i%4 of the call with offset i//4 in its stream
+    seed, stream = 0xDEADBEEF12345, 1
+    idx = np.arange(40, dtype=np.uint64)
+    got = uniform_words(seed, stream, idx)
+    ref = torch_philox([(seed, stream, i) for i in range(10)]).reshape(-1)
+    assert np.array_equal(got.astype(np.uint64), ref)
