@@ -1,0 +1,86 @@
+"""ctypes binding of libmxfp4.so: argument marshalling only.
+
+Every step of the quantizer and the GEMM runs in the HIP kernels behind the C
+ABI declared in include/mxfp4.h; nothing here computes.  Loading fails loudly
+when the library has not been built.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
+
+MX_OK, MX_ERR_INVALID, MX_ERR_UNSUPPORTED, MX_ERR_DEVICE = 0, 1, 2, 3
+GRID = {"e2m1": 0, "e1m2": 1}
+ROUND = {"rtne": 0, "sr": 1}
+AXIS = {"row": 1, "col": 2, "both": 3}
+HAD = {"none": 0, "det": 1, "rand": 2}
+OUT = {"f32": 0, "bf16": 1}
+
+EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_status_str", "mx_version")
+
+
+class MXError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__("%s returned %s" % (fn, status_str(status)))
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmxfp4.so is not built; run python -m block_scaled_fp4_hadamard_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, u64, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p
+        qp = ctypes.POINTER(QTensorC)
+        L.mx_quantize.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, qp, qp, vp]
+        L.mx_quantize.restype = ctypes.c_int
+        L.mx_hadamard_quantize.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, i32, i32, u64, qp, qp, vp]
+        L.mx_hadamard_quantize.restype = ctypes.c_int
+        L.mx_gemm.argtypes = [qp, qp, i64, i64, i64, i32, i32, vp, i64, i32, vp]
+        L.mx_gemm.restype = ctypes.c_int
+        L.mx_status_str.argtypes = [ctypes.c_int]
+        L.mx_status_str.restype = ctypes.c_char_p
+        L.mx_version.argtypes = []
+        L.mx_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().mx_status_str(status).decode()
+
+
+def check(status, fn):
+    if status != MX_OK:
+        raise MXError(status, fn)
+
+
+def qtensor(codes_ptr, ld_codes, scales_ptr, ld_scales):
+    return QTensorC(codes_ptr, ld_codes, scales_ptr, ld_scales)
+
+
+def mx_quantize(x_ptr, rows, cols, ld_x, block, grid, rnd, axis, seed, row_q, col_q, stream):
+    return lib().mx_quantize(x_ptr, rows, cols, ld_x, block, grid, rnd, axis, seed,
+                             ctypes.byref(row_q) if row_q is not None else None,
+                             ctypes.byref(col_q) if col_q is not None else None, stream)
+
+
+def mx_hadamard_quantize(x_ptr, rows, cols, ld_x, block, grid, rnd, axis, seed, had_n, had_kind, had_seed,
+                         row_q, col_q, stream):
+    return lib().mx_hadamard_quantize(x_ptr, rows, cols, ld_x, block, grid, rnd, axis, seed, had_n, had_kind,
+                                      had_seed, ctypes.byref(row_q) if row_q is not None else None,
+                                      ctypes.byref(col_q) if col_q is not None else None, stream)
+
+
+def mx_gemm(a_q, b_q, M, N, K, grid, block, c_ptr, ldc, out, stream):
+    return lib().mx_gemm(ctypes.byref(a_q), ctypes.byref(b_q), M, N, K, grid, block, c_ptr, ldc, out, stream)

@@ -1,0 +1,102 @@
+"""PyTorch-facing wrappers over the C ABI: they allocate outputs with torch on
+the tensor's device and launch on torch's current stream.  No arithmetic of
+the method happens here.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class QTensor:
+    """A block-scaled 4-bit operand: L lines of length K, K-contiguous.
+
+    codes  uint8 (L, K/2): element 2j of a line in the low nibble of byte j
+    scales uint8 (L, K/32): E8M0 exponent byte per 32-element block
+    """
+    codes: torch.Tensor
+    scales: torch.Tensor
+    grid: str = "e2m1"
+
+    @property
+    def lines(self):
+        return self.codes.shape[0]
+
+    @property
+    def k(self):
+        return self.codes.shape[1] * 2
+
+    def c_struct(self):
+        return _lib.qtensor(self.codes.data_ptr(), self.codes.stride(0),
+                            self.scales.data_ptr(), self.scales.stride(0))
+
+
+def _stream(dev):
+    return ctypes_void(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def ctypes_void(handle):
+    return handle if handle else None
+
+
+def _bits_view(x):
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16)
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError("x must be bfloat16 (or its 16-bit patterns), got %s" % x.dtype)
+
+
+def empty_qtensor(lines, k, device, grid="e2m1", block=32):
+    return QTensor(torch.empty((lines, k // 2), dtype=torch.uint8, device=device),
+                   torch.empty((lines, k // block), dtype=torch.uint8, device=device), grid)
+
+
+def quantize(x, axis="row", grid="e2m1", rounding="rtne", seed=0, had_n=0, had_kind="det", had_seed=0,
+             block=32, row_out=None, col_out=None):
+    """Quantize a 2-D bf16 CUDA tensor; returns {"row": QTensor, "col": QTensor} as requested.
+
+    had_n 0 means no rotation; otherwise 16 or 32 with had_kind "det" or "rand".
+    """
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    xb = _bits_view(x)
+    rows, cols = x.shape
+    dev = x.device
+    do_row, do_col = axis in ("row", "both"), axis in ("col", "both")
+    out = {}
+    rq = cq = None
+    if do_row:
+        out["row"] = row_out if row_out is not None else empty_qtensor(rows, cols, dev, grid, block)
+        rq = out["row"].c_struct()
+    if do_col:
+        out["col"] = col_out if col_out is not None else empty_qtensor(cols, rows, dev, grid, block)
+        cq = out["col"].c_struct()
+    stream = _stream(dev)
+    if had_n:
+        st = _lib.mx_hadamard_quantize(xb.data_ptr(), rows, cols, xb.stride(0), block, _lib.GRID[grid],
+                                       _lib.ROUND[rounding], _lib.AXIS[axis], seed, had_n, _lib.HAD[had_kind],
+                                       had_seed, rq, cq, stream)
+        _lib.check(st, "mx_hadamard_quantize")
+    else:
+        st = _lib.mx_quantize(xb.data_ptr(), rows, cols, xb.stride(0), block, _lib.GRID[grid],
+                              _lib.ROUND[rounding], _lib.AXIS[axis], seed, rq, cq, stream)
+        _lib.check(st, "mx_quantize")
+    return out
+
+
+def gemm(a, b, out_dtype=torch.float32, out=None, grid=None):
+    """C = A B^T on the decoded operands (M x N), fp32 accumulation, fp32 or bf16 output."""
+    if a.k != b.k:
+        raise ValueError("operands disagree on K: %d vs %d" % (a.k, b.k))
+    grid = grid or a.grid
+    M, N, K = a.lines, b.lines, a.k
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    kind = {torch.float32: "f32", torch.bfloat16: "bf16"}[out.dtype]
+    st = _lib.mx_gemm(a.c_struct(), b.c_struct(), M, N, K, _lib.GRID[grid], 32, out.data_ptr(), out.stride(0),
+                      _lib.OUT[kind], _stream(out.device))
+    _lib.check(st, "mx_gemm")
+    return out

@@ -1,0 +1,160 @@
+// C ABI of the MX quantizer and GEMM: argument validation, the random sign
+// vector of the randomized Hadamard rotation, and the kernel launches.
+// Validation happens before any HIP call, so argument errors never touch the
+// device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "mx_kernels.h"
+
+namespace {
+
+constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u, kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+
+// Host Philox4x32-10, word 0 only: the sign vector of the randomized rotation
+// is word 0 of the draw with counter (0, 0, 2, 0) under key had_seed.
+uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)c0 * kM0, p1 = (uint64_t)c2 * kM1;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += kW0;
+    k1 += kW1;
+  }
+  return c0;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+mx_status check_qtensor(const mx_qtensor* q, int64_t lines, int64_t k, int32_t block) {
+  if (q == nullptr || q->codes == nullptr || q->scales == nullptr) return MX_ERR_INVALID;
+  if (!aligned16(q->codes) || q->ld_codes % 16 != 0) return MX_ERR_INVALID;
+  if (q->ld_codes < k / 2 || q->ld_scales < k / block) return MX_ERR_INVALID;
+  if (lines > 1 && (q->ld_codes <= 0 || q->ld_scales <= 0)) return MX_ERR_INVALID;
+  return MX_OK;
+}
+
+mx_status quantize_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block, int grid,
+                        int round, int axis, uint64_t seed, int had_n, int had_kind, uint64_t had_seed,
+                        const mx_qtensor* row_out, const mx_qtensor* col_out, void* stream) {
+  if (rows < 0 || cols < 0) return MX_ERR_INVALID;
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (round != MX_ROUND_RTNE && round != MX_ROUND_SR) return MX_ERR_INVALID;
+  if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL && axis != MX_AXIS_BOTH) return MX_ERR_INVALID;
+  if (had_kind != MX_HAD_NONE && had_kind != MX_HAD_DET && had_kind != MX_HAD_RAND) return MX_ERR_INVALID;
+  if (had_kind == MX_HAD_NONE) had_n = 0;
+  else if (had_n != 16 && had_n != 32) return MX_ERR_INVALID;
+  if (block != 16 && block != 32) return MX_ERR_INVALID;
+  if (had_n > block) return MX_ERR_INVALID;
+  const bool do_row = (axis & MX_AXIS_ROW) != 0, do_col = (axis & MX_AXIS_COL) != 0;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (x == nullptr || !aligned16(x)) return MX_ERR_INVALID;
+  if (ld_x < cols || ld_x % 8 != 0 || cols % 8 != 0) return MX_ERR_INVALID;
+  if (do_row) {
+    if (cols % block != 0) return MX_ERR_INVALID;
+    mx_status s = check_qtensor(row_out, rows, cols, block);
+    if (s != MX_OK) return s;
+  }
+  if (do_col) {
+    if (rows % block != 0) return MX_ERR_INVALID;
+    mx_status s = check_qtensor(col_out, cols, rows, block);
+    if (s != MX_OK) return s;
+  }
+  if (block != 32) return MX_ERR_UNSUPPORTED;
+  mx::QuantParams p{};
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld_x = ld_x;
+  if (do_row) {
+    p.row_codes = row_out->codes;
+    p.ld_row_codes = row_out->ld_codes;
+    p.row_scales = row_out->scales;
+    p.ld_row_scales = row_out->ld_scales;
+  }
+  if (do_col) {
+    p.col_codes = col_out->codes;
+    p.ld_col_codes = col_out->ld_codes;
+    p.col_scales = col_out->scales;
+    p.ld_col_scales = col_out->ld_scales;
+  }
+  p.seed = seed;
+  p.sign_mask = 0u;
+  const bool rht = had_kind == MX_HAD_RAND;
+  if (rht) {
+    const uint32_t w0 = philox_word0(0u, 0u, 2u, 0u, (uint32_t)had_seed, (uint32_t)(had_seed >> 32));
+    p.sign_mask = had_n == 32 ? w0 : (w0 & 0xFFFFu);
+  }
+  hipError_t e = mx::launch_quant(p, had_n, rht, grid, round, do_row, do_col, (hipStream_t)stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block, mx_grid grid,
+                      mx_round round, mx_axis axis, uint64_t seed, const mx_qtensor* row_out,
+                      const mx_qtensor* col_out, void* hip_stream) {
+  return quantize_impl(x, rows, cols, ld_x, block, grid, round, axis, seed, 0, MX_HAD_NONE, 0, row_out, col_out,
+                       hip_stream);
+}
+
+mx_status mx_hadamard_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block,
+                               mx_grid grid, mx_round round, mx_axis axis, uint64_t seed, int32_t had_n,
+                               mx_had had_kind, uint64_t had_seed, const mx_qtensor* row_out,
+                               const mx_qtensor* col_out, void* hip_stream) {
+  if (had_kind == MX_HAD_NONE) return MX_ERR_INVALID;
+  return quantize_impl(x, rows, cols, ld_x, block, grid, round, axis, seed, had_n, had_kind, had_seed, row_out,
+                       col_out, hip_stream);
+}
+
+mx_status mx_gemm(const mx_qtensor* a, const mx_qtensor* b, int64_t M, int64_t N, int64_t K, mx_grid grid,
+                  int32_t block, void* c, int64_t ldc, mx_out out, void* hip_stream) {
+  if (M < 0 || N < 0 || K <= 0) return MX_ERR_INVALID;
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (out != MX_OUT_F32 && out != MX_OUT_BF16) return MX_ERR_INVALID;
+  if (block != 16 && block != 32) return MX_ERR_INVALID;
+  if (K % block != 0) return MX_ERR_INVALID;
+  if (M == 0 || N == 0) return MX_OK;
+  mx_status s = check_qtensor(a, M, K, block);
+  if (s != MX_OK) return s;
+  s = check_qtensor(b, N, K, block);
+  if (s != MX_OK) return s;
+  const uintptr_t esize = out == MX_OUT_F32 ? 4u : 2u;
+  if (c == nullptr || ((uintptr_t)c % esize) != 0 || ldc < N) return MX_ERR_INVALID;
+  if (block != 32) return MX_ERR_UNSUPPORTED;
+  mx::GemmParams p{};
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.b_codes = b->codes;
+  p.b_scales = b->scales;
+  p.lda_codes = a->ld_codes;
+  p.lda_scales = a->ld_scales;
+  p.ldb_codes = b->ld_codes;
+  p.ldb_scales = b->ld_scales;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  hipError_t e = mx::launch_gemm(p, grid, out, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
+const char* mx_status_str(mx_status status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_INVALID: return "MX_ERR_INVALID: invalid argument";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED: valid request not implemented";
+    case MX_ERR_DEVICE: return "MX_ERR_DEVICE: HIP runtime error";
+  }
+  return "unknown mx_status";
+}
+
+int32_t mx_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+// Device-side helpers shared by the quantizer kernels: Philox4x32-10, the
+// exact fallback for the Hadamard sums, and small bit utilities.
+// gfx950 (CDNA4) only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies on a 128-bit counter, Weyl-bumped 64-bit key.  The key
+// is wave-uniform (it lives in SGPRs); each lane runs its own counter.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)c0 * kPhiloxM0;
+    const uint64_t p1 = (uint64_t)c2 * kPhiloxM1;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+// ---------------------------------------------------------------------------
+// Exact Hadamard sums for the rare chunks where float64 butterflies could
+// round (inputs spanning more than 40 binades) or hold non-finite values.
+//
+// S_i = sum_j sgn(i, j) x_j with x_j bf16.  Each finite x_j is an integer
+// significand (<= 8 bits) times 2^(max(E,1) - 134); placed at bit
+// max(E,1) - 1 of a fixed-point accumulator whose bit 0 weighs 2^-133, the
+// whole bf16 range fits in 9 limbs of 32 bits (signed int64 per limb so that
+// 32 terms never overflow before the carry pass).  The result is rounded to
+// the nearest fp32, ties to even (values below 2^-126 are exact subnormals).
+
+__device__ __forceinline__ float rn32_from_limbs(int64_t (&acc)[9]) {
+  // carry-propagate into canonical 32-bit limbs with a signed top limb
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    const int64_t c = acc[l] >> 32;            // arithmetic shift: floor division
+    acc[l] -= c * 4294967296LL;
+    acc[l + 1] += c;
+  }
+  uint32_t u[9];
+  const bool neg = acc[8] < 0;
+  {
+    // magnitude: two's complement negate over the limbs when negative
+    uint32_t carry = 1;
+#pragma unroll
+    for (int l = 0; l < 9; ++l) {
+      const uint32_t w = (uint32_t)(acc[l] & 0xFFFFFFFFLL);
+      if (neg) {
+        const uint64_t s = (uint64_t)(~w) + carry;
+        u[l] = (uint32_t)s;
+        carry = (uint32_t)(s >> 32);
+      } else {
+        u[l] = w;
+      }
+    }
+  }
+  // most significant set bit
+  int msb = -1;
+#pragma unroll
+  for (int l = 0; l < 9; ++l)
+    if (u[l] != 0u) msb = l * 32 + 31 - __clz((int)u[l]);
+  const uint32_t sbit = neg ? 0x80000000u : 0u;
+  if (msb < 0) return 0.0f;                    // exact zero: +0
+  // read a 64-bit window of the magnitude ending at bit msb
+  auto bit_window = [&](int lo) -> uint64_t {  // bits [lo, lo+64) (lo may be negative)
+    uint64_t r = 0;
+#pragma unroll
+    for (int l = 0; l < 9; ++l) {
+      const int pos = l * 32 - lo;             // where limb l lands in the window
+      if (pos >= 64 || pos <= -32) continue;
+      const uint64_t w = u[l];
+      r |= pos >= 0 ? (w << pos) : (w >> (-pos));
+    }
+    return r;
+  };
+  if (msb < 7) {                               // below 2^-126: an exact subnormal
+    return __uint_as_float(sbit | (u[0] << 16));
+  }
+  const int exp_unb = msb - 133;               // floor(log2 |S|)
+  if (exp_unb > 127) return __uint_as_float(sbit | 0x7F800000u);
+  // 24 kept bits [msb-23, msb], round bit msb-24, sticky below
+  const uint64_t win = bit_window(msb - 40);   // bit k of win = bit (msb-40+k)
+  uint32_t mant = (uint32_t)(win >> 17) & 0xFFFFFFu;    // bits msb-23..msb
+  const uint32_t rbit = (uint32_t)(win >> 16) & 1u;
+  bool sticky = (win & 0xFFFFull) != 0;
+  // bits below msb-40 also feed the sticky bit
+  const int below = msb - 40;
+  if (below > 0) {
+#pragma unroll
+    for (int l = 0; l < 9; ++l) {
+      const int lo = l * 32;
+      if (lo >= below) continue;
+      const int nb = below - lo;               // bits of limb l below the window
+      const uint32_t m = nb >= 32 ? 0xFFFFFFFFu : ((1u << nb) - 1u);
+      sticky |= (u[l] & m) != 0u;
+    }
+  }
+  int e = exp_unb;
+  if (rbit && (sticky || (mant & 1u))) {
+    mant += 1u;
+    if (mant == 0x1000000u) { mant = 0x800000u; e += 1; }
+  }
+  if (e > 127) return __uint_as_float(sbit | 0x7F800000u);
+  return __uint_as_float(sbit | ((uint32_t)(e + 127) << 23) | (mant & 0x7FFFFFu));
+}
+
+// Exact S_i for output i of a chunk of N bf16 values (bit patterns in xb[]),
+// with sign vector mask (bit j set: x_j negated).  All inputs finite.
+template <int N>
+__device__ __forceinline__ float exact_hadamard_rn32(const uint32_t (&xb)[N], int i, uint32_t mask) {
+  int64_t acc[9];
+#pragma unroll
+  for (int l = 0; l < 9; ++l) acc[l] = 0;
+#pragma unroll 1
+  for (int j = 0; j < N; ++j) {
+    const uint32_t b = xb[j];
+    const uint32_t ef = (b >> 7) & 0xFFu;
+    const uint32_t sig = ef ? ((b & 0x7Fu) | 0x80u) : (b & 0x7Fu);
+    if (sig == 0u) continue;
+    const int p = (int)(ef ? ef : 1u) - 1;                 // 0 .. 253
+    const int L = p >> 5, off = p & 31;
+    const uint64_t v = (uint64_t)sig << off;
+    const bool neg = (((b >> 15) & 1u) ^ ((mask >> j) & 1u) ^ (__popc((unsigned)(i & j)) & 1u)) != 0u;
+    const int64_t lo = (int64_t)(v & 0xFFFFFFFFull), hi = (int64_t)(v >> 32);
+#pragma unroll
+    for (int l = 0; l < 9; ++l) {
+      int64_t add = (l == L) ? lo : ((l == L + 1) ? hi : 0);
+      acc[l] += neg ? -add : add;
+    }
+  }
+  return rn32_from_limbs(acc);
+}
+
+}  // namespace mx

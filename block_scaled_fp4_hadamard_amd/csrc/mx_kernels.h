@@ -1,0 +1,41 @@
+// Internal interface between the C ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "../../include/mxfp4.h"
+
+namespace mx {
+
+struct QuantParams {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  uint8_t* row_codes;
+  int64_t ld_row_codes;
+  uint8_t* row_scales;
+  int64_t ld_row_scales;
+  uint8_t* col_codes;
+  int64_t ld_col_codes;
+  uint8_t* col_scales;
+  int64_t ld_col_scales;
+  uint64_t seed;
+  uint32_t sign_mask;   // bit j set: input j of every Hadamard chunk is negated
+  int32_t n_row_tiles, n_col_tiles, n_row_groups;   // filled by launch_quant
+};
+
+hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int round, bool do_row, bool do_col,
+                        hipStream_t s);
+
+struct GemmParams {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int64_t lda_codes, lda_scales, ldb_codes, ldb_scales;
+  int64_t M, N, K;
+  void* c;
+  int64_t ldc;
+};
+
+hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s);
+
+}  // namespace mx

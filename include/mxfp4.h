@@ -1,0 +1,148 @@
+/*
+ * mxfp4.h - C ABI of the MI355X (gfx950) block-scaled 4-bit quantizer and GEMM.
+ *
+ * What is computed (by page title and section):
+ *  - "Pre-addestramento di Modelli Linguistici di Grandi Dimensioni con MXFP4",
+ *    Metodologia: the three GEMMs of a linear layer's training step (Fprop,
+ *    Dgrad, Wgrad) in MXFP4, optionally after a deterministic H16/H32 or a
+ *    randomized Hadamard rotation; stochastic rounding as an alternative.
+ *  - "Ripensare il Bias di Shrinkage nel Pretraining di LLM in FP4",
+ *    Problematica and Metodologia 2: E2M1 under round-to-nearest-even, and the
+ *    uniform E1M2/INT4 grid of the UFP4 recipe.
+ *  - "MXNorm: Reusing MXFP block scales ...", Sommario tecnico 2: one shared
+ *    scale per block derived from the block's absolute maximum.
+ *  - "Résumé Technique : TetraJet-v2", section 2.A: stochastic rounding with
+ *    E[round(x)] = x.
+ *
+ * Data layout (all row-major, strides in the units named):
+ *  - Input x: bf16 bit patterns, x[r * ld_x + c], 0 <= r < rows, 0 <= c < cols.
+ *  - A quantized operand (mx_qtensor) of L lines of length K:
+ *      codes [L][K/2] bytes, line stride ld_codes bytes; element 2j of a line in
+ *      the low nibble of byte j; nibble bit 3 = sign, bits 2..0 = magnitude code
+ *      (E2M1: 0,0.5,1,1.5,2,3,4,6; E1M2: k/4);
+ *      scales [L][K/block] bytes (E8M0: value 2^(byte-127), 0xFF = NaN block),
+ *      line stride ld_scales bytes.
+ *  - Row-wise output: lines = rows, K = cols (blocks run along a row).
+ *    Column-wise output: lines = cols, K = rows: the quantized transpose, so
+ *    every GEMM operand is K-contiguous.
+ *
+ * The cast: e = clamp(floor(log2 amax) - emax, -127, 127) per block of 32
+ * (emax 2 for E2M1, 0 for E1M2; amax 0 gives -127); v = |y| / 2^e goes to the
+ * grid by round-to-nearest-even (ties to the even code, saturating at the top
+ * level) or by stochastic rounding: with lo <= v < hi adjacent levels,
+ * P = floor((v - lo) / (hi - lo) * 2^32), round up iff u < P, where u is word
+ * (i mod 4) of Philox4x32-10(key = seed, counter = (i div 4, stream, 0)) for
+ * the element at index i of the output's logical row-major order (row-wise:
+ * r*cols + c, stream 0; column-wise: c*rows + r, stream 1).  A block holding a
+ * non-finite value gets scale 0xFF and codes 0.
+ *
+ * The rotation (mx_hadamard_quantize): y = RN32(RN32(S) * RN32(1/sqrt(n)))
+ * per aligned chunk of n = 16 or 32 along the quantization axis, where S is
+ * the EXACT value of sum_j H[i][j] s_j x_j, H the Sylvester matrix
+ * (H[i][j] = (-1)^popcount(i & j)), s_j = +1 (MX_HAD_DET) or, for
+ * MX_HAD_RAND, s_j = -1 iff bit j of word 0 of
+ * Philox4x32-10(key = had_seed, counter = (0, 0, 2, 0)).  An exact zero sum
+ * gives +0; a chunk holding a non-finite input gives NaN outputs.
+ *
+ * Conventions:
+ *  - All pointers are caller-owned DEVICE pointers (the mx_qtensor structs
+ *    themselves are host memory, read before the call returns).  The library
+ *    allocates no memory and keeps no mutable global state; calls are
+ *    thread-safe.
+ *  - Every call is asynchronous on hip_stream (a hipStream_t; NULL = the
+ *    default stream).  Argument errors are reported synchronously, before
+ *    anything is launched.  A launch failure returns MX_ERR_DEVICE; faults
+ *    surface at the caller's next synchronization.
+ *  - Nothing throws across the ABI.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_INVALID = 1,      /* a null/misaligned pointer, a bad size or stride, an enum out of range */
+  MX_ERR_UNSUPPORTED = 2,  /* a valid request this library does not implement (e.g. block 16 GEMM) */
+  MX_ERR_DEVICE = 3        /* the HIP runtime refused a launch or query */
+} mx_status;
+
+typedef enum { MX_GRID_E2M1 = 0, MX_GRID_E1M2 = 1 } mx_grid;
+typedef enum { MX_ROUND_RTNE = 0, MX_ROUND_SR = 1 } mx_round;
+typedef enum { MX_AXIS_ROW = 1, MX_AXIS_COL = 2, MX_AXIS_BOTH = 3 } mx_axis;   /* bit mask */
+typedef enum { MX_HAD_NONE = 0, MX_HAD_DET = 1, MX_HAD_RAND = 2 } mx_had;
+typedef enum { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out;
+
+typedef struct {
+  uint8_t *codes;     /* device: [lines][K/2] packed 4-bit codes */
+  int64_t ld_codes;   /* bytes between lines; >= K/2, multiple of 16 */
+  uint8_t *scales;    /* device: [lines][K/block] E8M0 bytes */
+  int64_t ld_scales;  /* bytes between lines; >= K/block */
+} mx_qtensor;
+
+/*
+ * mx_quantize: block-scaled 4-bit quantization of a bf16 matrix, no rotation.
+ *   x          device, 16-byte aligned, bf16 bit patterns
+ *   rows, cols >= 0 (either 0: nothing to do, MX_OK); cols % 8 == 0;
+ *              cols % block == 0 if the row-wise output is requested,
+ *              rows % block == 0 if the column-wise output is requested
+ *   ld_x       elements between rows; >= cols, multiple of 8
+ *   block      32 (the MX block; 16 returns MX_ERR_UNSUPPORTED)
+ *   grid       MX_GRID_E2M1 or MX_GRID_E1M2
+ *   round      MX_ROUND_RTNE or MX_ROUND_SR (seed keys the Philox draws)
+ *   axis       which outputs to write; row_out / col_out must be non-null for
+ *              the requested ones (codes 16-byte aligned) and are ignored
+ *              otherwise
+ * Both outputs of MX_AXIS_BOTH come from one pass over x.
+ */
+mx_status mx_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                      int32_t block, mx_grid grid, mx_round round, mx_axis axis,
+                      uint64_t seed, const mx_qtensor *row_out, const mx_qtensor *col_out,
+                      void *hip_stream);
+
+/*
+ * mx_hadamard_quantize: as mx_quantize, after a block Hadamard rotation of
+ * order had_n (16 or 32, dividing block) along each output's quantization
+ * axis (row-wise: along a row; column-wise: along a column).  had_kind
+ * MX_HAD_DET or MX_HAD_RAND (had_seed draws the sign vector; the same vector
+ * serves both outputs, so the rotation cancels in a GEMM whose two operands
+ * were rotated with the same had_n, had_kind and had_seed).
+ */
+mx_status mx_hadamard_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                               int32_t block, mx_grid grid, mx_round round, mx_axis axis,
+                               uint64_t seed, int32_t had_n, mx_had had_kind, uint64_t had_seed,
+                               const mx_qtensor *row_out, const mx_qtensor *col_out,
+                               void *hip_stream);
+
+/*
+ * mx_gemm: C[m][n] = sum_k A[m][k] * B[n][k] on the decoded values, with fp32
+ * accumulation ("Pre-addestramento ... con MXFP4", Metodologia: MXFP4 GEMMs on
+ * native FP4 matrix units).
+ *   a          M lines of length K (codes [M][K/2], scales [M][K/32])
+ *   b          N lines of length K (codes [N][K/2], scales [N][K/32])
+ *   M, N, K    >= 0 (any 0: nothing to do; K == 0 is rejected); K % 32 == 0
+ *   grid       the grid both operands were quantized to (E1M2 runs as exact
+ *              FP6 E2M3 on the matrix units)
+ *   block      32
+ *   c          device, row-major [M][ldc] fp32 or bf16 (round to nearest even
+ *              of the fp32 result); aligned to its element size, ldc >= N
+ */
+mx_status mx_gemm(const mx_qtensor *a, const mx_qtensor *b, int64_t M, int64_t N, int64_t K,
+                  mx_grid grid, int32_t block, void *c, int64_t ldc, mx_out out,
+                  void *hip_stream);
+
+/* A static, human-readable name for a status code. */
+const char *mx_status_str(mx_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

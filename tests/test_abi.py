@@ -1,0 +1,92 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching a device (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_fp4_hadamard_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmxfp4.so not built")
+
+FAKE = 0x10000          # an aligned non-null address; validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    assert _lib.status_str(0) == "MX_OK"
+    assert "INVALID" in _lib.status_str(1)
+    assert "UNSUPPORTED" in _lib.status_str(2)
+    assert "DEVICE" in _lib.status_str(3)
+    assert _lib.lib().mx_version() >= 100
+
+
+def q(ld_codes=64, ld_scales=4, codes=FAKE, scales=FAKE):
+    return _lib.qtensor(codes, ld_codes, scales, ld_scales)
+
+
+def quant(x=FAKE, rows=32, cols=128, ld=128, block=32, grid=0, rnd=0, axis=1, rq="d", cq="d"):
+    rq = q() if rq == "d" else rq
+    cq = q(ld_codes=16, ld_scales=1) if cq == "d" else cq
+    return _lib.mx_quantize(x, rows, cols, ld, block, grid, rnd, axis, 0, rq, cq, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), 1), (dict(cols=-5), 1), (dict(grid=7), 1), (dict(rnd=9), 1), (dict(axis=0), 1),
+    (dict(axis=4), 1), (dict(block=64), 1), (dict(x=0), 1), (dict(x=FAKE + 2), 1),
+    (dict(ld=100), 1), (dict(cols=120, ld=128), 1),          # row output needs cols % 32
+    (dict(cols=12, ld=16, axis=2), 1),                          # cols % 8
+    (dict(rows=40, axis=2), 1),                                 # column output needs rows % 32
+    (dict(rq=None), 1), (dict(rq=q(codes=FAKE + 8)), 1), (dict(rq=q(ld_codes=32)), 1),
+    (dict(rq=q(ld_codes=72)), 1), (dict(rq=q(ld_scales=2)), 1), (dict(rq=q(scales=0)), 1),
+    (dict(block=16, rq=q(ld_scales=8)), 2),                     # valid, not implemented
+    (dict(rows=0), 0), (dict(cols=0), 0),                       # empty: nothing to do
+])
+def test_quantize_validation(kw, want):
+    assert quant(**kw) == want
+
+
+def test_hadamard_validation():
+    L = _lib
+    def hq(had_n=32, kind=1, block=32):
+        return L.mx_hadamard_quantize(FAKE, 32, 128, 128, block, 0, 0, 1, 0, had_n, kind, 0, q(), None, None)
+    assert hq(had_n=8) == 1
+    assert hq(had_n=64) == 1
+    assert hq(kind=0) == 1        # the rotating entry point needs a rotation
+    assert hq(kind=5) == 1
+    assert hq(had_n=32, block=16) == 1   # the rotation must fit in a block
+
+
+def gemm(M=64, N=64, K=128, grid=0, block=32, c=FAKE, ldc=64, out=0, a="d", b="d"):
+    a = q(ld_codes=64, ld_scales=4) if a == "d" else a
+    b = q(ld_codes=64, ld_scales=4) if b == "d" else b
+    return _lib.mx_gemm(a, b, M, N, K, grid, block, c, ldc, out, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(K=0), 1), (dict(K=100), 1), (dict(M=-1), 1), (dict(grid=3), 1), (dict(out=2), 1),
+    (dict(c=0), 1), (dict(c=FAKE + 2), 1), (dict(c=FAKE + 3, out=1), 1), (dict(ldc=60), 1),
+    (dict(a=q(ld_codes=32)), 1), (dict(b=q(scales=0)), 1), (dict(block=8), 1),
+    (dict(block=16, a=q(ld_scales=8), b=q(ld_scales=8)), 2), (dict(M=0), 0), (dict(N=0), 0),
+])
+def test_gemm_validation(kw, want):
+    assert gemm(**kw) == want

@@ -1,0 +1,90 @@
+"""GPU parity of the block-scaled GEMM against the oracle's float64 GEMM."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.gemm import gemm_ref
+from oracle.quantize import quantize_ref
+from block_scaled_fp4_hadamard_amd import QTensor, quantize, gemm
+from block_scaled_fp4_hadamard_amd import synth
+from gpu_helpers import announce, to_gpu_bits, qt_to_np, assert_bytes_equal, assert_gemm_close
+
+pytestmark = pytest.mark.gpu
+
+
+def random_operand(rng, lines, k, lo=118, hi=136):
+    codes = rng.integers(0, 256, (lines, k // 2), dtype=np.uint8)
+    scales = rng.integers(lo, hi, (lines, k // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def run_gemm(a, b, grid, out_dtype=torch.float32):
+    qa = QTensor(torch.from_numpy(a[0]).cuda(), torch.from_numpy(a[1]).cuda(), grid)
+    qb = QTensor(torch.from_numpy(b[0]).cuda(), torch.from_numpy(b[1]).cuda(), grid)
+    c = gemm(qa, qb, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (300, 200, 160), (513, 257, 1088), (32, 32, 32),
+                                   (1, 7, 64), (640, 520, 4096)])
+def test_gemm_random_operands(grid, m, n, k):
+    announce("gemm random %s %dx%dx%d" % (grid, m, n, k))
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c = run_gemm(a, b, grid)
+    c_ref, g = gemm_ref(*a, *b, k, grid)
+    assert_gemm_close(c, c_ref, g, "gemm %s %dx%dx%d" % (grid, m, n, k))
+
+
+def test_gemm_bf16_output_is_rounded_fp32():
+    rng = np.random.default_rng(3)
+    a = random_operand(rng, 384, 512)
+    b = random_operand(rng, 320, 512)
+    c32 = run_gemm(a, b, "e2m1", torch.float32)
+    c16 = run_gemm(a, b, "e2m1", torch.bfloat16)
+    want = torch.from_numpy(c32).to(torch.bfloat16).float().numpy()   # torch's RNE cast on the CPU
+    assert np.array_equal(c16, want)
+    c_ref, g = gemm_ref(*a, *b, 512, "e2m1")
+    assert_gemm_close(c16, c_ref, g, "bf16", bf16=True)
+
+
+def test_tiny_workload_end_to_end():
+    """256x256 A (2 outlier columns) times W^T: oracle-quantized operands, GPU bytes must match."""
+    d = synth.tiny()
+    announce("tiny end to end")
+    qa = quantize(to_gpu_bits(d["a"]), axis="row")["row"]
+    qw = quantize(to_gpu_bits(d["w"]), axis="row")["row"]
+    c = gemm(qa, qw)
+    torch.cuda.synchronize()
+    ra = quantize_ref(d["a"], "row")["row"]
+    rw = quantize_ref(d["w"], "row")["row"]
+    assert_bytes_equal(qt_to_np(qa)[0], ra[0], "A codes")
+    assert_bytes_equal(qt_to_np(qw)[0], rw[0], "W codes")
+    c_ref, g = gemm_ref(*ra, *rw, 256, "e2m1")
+    assert_gemm_close(c.cpu().numpy(), c_ref, g, "tiny")
+
+
+def test_fprop_qkv_full_size_sampled():
+    """8192x4096 X and 6144x4096 W, H16 on K, RTNE; Y = X W^T in bf16 and fp32 on sampled outputs."""
+    d = synth.fprop_qkv()
+    announce("fprop qkv full size")
+    qx = quantize(to_gpu_bits(d["x"]), axis="row", had_n=16)["row"]
+    qw = quantize(to_gpu_bits(d["w"]), axis="row", had_n=16)["row"]
+    y16 = gemm(qx, qw, out_dtype=torch.bfloat16)
+    y32 = gemm(qx, qw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rx = quantize_ref(d["x"], "row", had_n=16)["row"]
+    rw = quantize_ref(d["w"], "row", had_n=16)["row"]
+    assert_bytes_equal(qt_to_np(qx)[0], rx[0], "X codes")
+    assert_bytes_equal(qt_to_np(qx)[1], rx[1], "X scales")
+    assert_bytes_equal(qt_to_np(qw)[0], rw[0], "W codes")
+    assert_bytes_equal(qt_to_np(qw)[1], rw[1], "W scales")
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([rng.choice(8192, 96, replace=False), [0, 8191]])
+    cols = np.concatenate([rng.choice(6144, 96, replace=False), [0, 6143]])
+    c_ref, g = gemm_ref(*rx, *rw, 4096, "e2m1", rows=rows, cols=cols)
+    assert_gemm_close(y32[rows][:, cols].cpu().numpy(), c_ref, g, "fprop fp32")
+    assert_gemm_close(y16[rows][:, cols].float().cpu().numpy(), c_ref, g, "fprop bf16", bf16=True)

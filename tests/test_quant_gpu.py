@@ -1,0 +1,111 @@
+"""GPU parity of the fused quantizer against the oracle: codes and scales bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.quantize import quantize_ref
+from block_scaled_fp4_hadamard_amd import quantize
+from block_scaled_fp4_hadamard_amd import synth
+from gpu_helpers import announce, to_gpu_bits, qt_to_np, assert_bytes_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def check(bits, name, **kw):
+    announce("%s shape=%s %s" % (name, bits.shape, kw))
+    out = quantize(to_gpu_bits(bits), **kw)
+    torch.cuda.synchronize()
+    ref = quantize_ref(bits, **kw)
+    assert set(out) == set(ref)
+    for key in ref:
+        gc, gs = qt_to_np(out[key])
+        assert_bytes_equal(gs, ref[key][1], "%s %s scales" % (name, key))
+        assert_bytes_equal(gc, ref[key][0], "%s %s codes" % (name, key))
+
+
+def test_tiny_workload_rowwise_rtne():
+    d = synth.tiny()
+    for name in ("a", "w"):
+        check(d[name], "tiny." + name, axis="row")
+
+
+ROTATIONS = [(0, "det"), (16, "det"), (32, "det"), (16, "rand"), (32, "rand")]
+
+
+@pytest.mark.parametrize("had_n,had_kind", ROTATIONS)
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_both_axes_several_tiles_ragged_cols(had_n, had_kind, grid, rounding):
+    # 96 x 544: 3 row tiles, 3 column tiles (the last holds 32 of 256 columns)
+    rng = np.random.default_rng(100 + had_n)
+    bits = synth.activation(96, 544, rng)
+    check(bits, "both", axis="both", grid=grid, rounding=rounding, seed=7, had_n=had_n, had_kind=had_kind,
+          had_seed=12345)
+
+
+@pytest.mark.parametrize("had_n", [0, 32])
+def test_row_only_ragged_rows(had_n):
+    rng = np.random.default_rng(5)
+    bits = synth.activation(70, 320, rng)
+    check(bits, "row-ragged", axis="row", had_n=had_n, rounding="sr", seed=3)
+    check(bits, "row-ragged", axis="row", had_n=had_n)
+
+
+@pytest.mark.parametrize("had_n", [0, 16])
+def test_col_only_ragged_cols(had_n):
+    rng = np.random.default_rng(6)
+    bits = synth.gradient(64, 264, rng)
+    check(bits, "col-ragged", axis="col", had_n=had_n, rounding="sr", seed=9)
+    check(bits, "col-ragged", axis="col", had_n=had_n, grid="e1m2")
+
+
+def edge_tensor():
+    """64 x 512: each 32x256 tile holds a different kind of trouble."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    # tile (0,0): zeros, -0, subnormals, blocks that are entirely zero
+    x[0:32, 0:256][rng.random((32, 256)) < 0.3] = 0.0
+    x[0, :32] = 0.0
+    x[1, :32] = -0.0
+    x[2, :32] = np.float32(1e-40) * rng.standard_normal(32).astype(np.float32)
+    x[:32, 40] = -0.0
+    # tile (0,1): a span far beyond 40 binades (exact fixed-point sums)
+    x[0:32, 256:512] *= np.exp2(rng.integers(-100, 60, (32, 256))).astype(np.float32)
+    # tile (1,0): non-finite inputs in a few blocks
+    x[40, 5] = np.inf
+    x[41, 70] = -np.inf
+    x[50, 200] = np.nan
+    # tile (1,1): values near the top of the range, and exact cancellation
+    x[32:64, 256:288] = 3.0e38
+    x[33, 256:288] = -3.0e38
+    x[34, 256:272] = 1.0
+    x[34, 272:288] = -1.0
+    bits = synth.f32_to_bf16_bits(np.nan_to_num(x, nan=0.0, posinf=0.0, neginf=0.0))
+    bits[40, 5], bits[41, 70], bits[50, 200] = 0x7F80, 0xFF80, 0x7FC1
+    return bits
+
+
+@pytest.mark.parametrize("had_n,had_kind", ROTATIONS)
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_edge_cases(had_n, had_kind, rounding):
+    bits = edge_tensor()
+    for grid in ("e2m1", "e1m2"):
+        check(bits, "edge", axis="both", grid=grid, rounding=rounding, seed=21, had_n=had_n, had_kind=had_kind,
+              had_seed=99)
+
+
+def test_repeatable():
+    bits = synth.activation(64, 512, np.random.default_rng(1))
+    x = to_gpu_bits(bits)
+    a = quantize(x, axis="both", rounding="sr", seed=5, had_n=32)
+    b = quantize(x, axis="both", rounding="sr", seed=5, had_n=32)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k].codes, b[k].codes) and torch.equal(a[k].scales, b[k].scales)
+
+
+@pytest.mark.parametrize("rounding,seed", [("rtne", 0), ("sr", 1)])
+def test_quantizer_workload_full_size(rounding, seed):
+    """8192 x 4096 activations with 0.1% outlier channels, H32, both outputs: every byte."""
+    bits = synth.quant_x()
+    check(bits, "quant-full", axis="both", rounding=rounding, seed=seed, had_n=32, had_kind="det")
