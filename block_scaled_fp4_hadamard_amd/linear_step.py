@@ -1,0 +1,117 @@
+"""Quantization and GEMM schedule of linear layers' training steps in MXFP4.
+
+"Pre-addestramento ... con MXFP4", Metodologia: a linear layer Y = X W^T
+runs three GEMMs, forward (Fprop), activation gradient (Dgrad) and weight
+gradient (Wgrad), each with both operands in MXFP4 and blocked along that
+GEMM's contraction axis:
+
+    Fprop  Y  = Q_row(X)  . Q_row(W)^T    M=T,   N=out, K=in   -> bf16
+    Dgrad  dX = Q_row(dY) . Q_col(W)^T    M=T,   N=in,  K=out  -> bf16
+    Wgrad  dW = Q_col(dY) . Q_col(X)^T    M=out, N=in,  K=T    -> fp32
+
+so every tensor is quantized once along each of its two axes (one
+MX_AXIS_BOTH launch).  "Ripensare il Bias di Shrinkage ...", Metodologia 2:
+the UFP4 recipe puts the random Hadamard transform on all three GEMMs and
+stochastic rounding on dY only, round-to-nearest-even elsewhere.  Both
+operands of a GEMM are rotated along its contraction axis with the same sign
+vector, so the rotation cancels in the product; one had_seed serves the block.
+
+This module only sequences library calls; every step runs in the HIP kernels.
+"""
+from dataclasses import dataclass, field
+
+import torch
+
+from . import api
+from .synth import LLAMA_LINEARS, LLAMA_INPUT_OF
+
+
+@dataclass
+class Launch:
+    label: str            # kernel family: quant.rtne, quant.sr, gemm.bf16, gemm.f32
+    name: str             # what it computes
+    fn: object            # zero-argument callable that enqueues the launch
+    bytes: int = 0        # algorithmic HBM bytes
+    flops: int = 0
+
+
+@dataclass
+class Recipe:
+    grid: str = "e2m1"
+    had_n: int = 32
+    had_kind: str = "rand"
+    had_seed: int = 20250
+    sr_on_dy: bool = True
+    sr_seed_base: int = 5000
+
+
+def quant_bytes(rows, cols, axes=2):
+    """bf16 read + per output 0.5 B/element codes and 1/32 B/element scales."""
+    return rows * cols * 2 + axes * (rows * cols // 2 + rows * cols // 32)
+
+
+@dataclass
+class LlamaBlockStep:
+    """All quantizations and the 21 GEMMs of one Llama block's seven linears.
+
+    tensors: dict of int16 CUDA tensors keyed like synth.llama_block().
+    """
+    tensors: dict
+    recipe: Recipe = field(default_factory=Recipe)
+
+    def __post_init__(self):
+        t = self.tensors
+        dev = next(iter(t.values())).device
+        r = self.recipe
+        self.q = {}
+        self.out = {}
+        tokens = t["x_attn"].shape[0]
+        self.launches = []
+        # quantize every input once (both axes), each weight, each gradient
+        names = sorted(set(LLAMA_INPUT_OF.values())) + ["w_" + n for n in LLAMA_LINEARS] + \
+            ["dy_" + n for n in LLAMA_LINEARS]
+        for ordinal, name in enumerate(names):
+            x = t[name]
+            rows, cols = x.shape
+            qrow = api.empty_qtensor(rows, cols, dev, r.grid)
+            qcol = api.empty_qtensor(cols, rows, dev, r.grid)
+            self.q[name] = {"row": qrow, "col": qcol}
+            sr = r.sr_on_dy and name.startswith("dy_")
+            rounding = "sr" if sr else "rtne"
+            seed = r.sr_seed_base + ordinal if sr else 0
+            fn = (lambda x=x, qrow=qrow, qcol=qcol, rounding=rounding, seed=seed:
+                  api.quantize(x, axis="both", grid=r.grid, rounding=rounding, seed=seed, had_n=r.had_n,
+                               had_kind=r.had_kind, had_seed=r.had_seed, row_out=qrow, col_out=qcol))
+            self.launches.append(Launch("quant." + rounding, "quantize " + name, fn, quant_bytes(rows, cols)))
+        for lin, (o, i) in LLAMA_LINEARS.items():
+            xq, wq, dq = self.q[LLAMA_INPUT_OF[lin]], self.q["w_" + lin], self.q["dy_" + lin]
+            y = torch.empty((tokens, o), dtype=torch.bfloat16, device=dev)
+            dx = torch.empty((tokens, i), dtype=torch.bfloat16, device=dev)
+            dw = torch.empty((o, i), dtype=torch.float32, device=dev)
+            self.out[lin] = {"y": y, "dx": dx, "dw": dw}
+            flops = 2 * tokens * o * i
+            self.launches.append(Launch("gemm.bf16", "fprop " + lin,
+                                        lambda a=xq["row"], b=wq["row"], c=y: api.gemm(a, b, out=c), 0, flops))
+            self.launches.append(Launch("gemm.bf16", "dgrad " + lin,
+                                        lambda a=dq["row"], b=wq["col"], c=dx: api.gemm(a, b, out=c), 0, flops))
+            self.launches.append(Launch("gemm.f32", "wgrad " + lin,
+                                        lambda a=dq["col"], b=xq["col"], c=dw: api.gemm(a, b, out=c), 0, flops))
+
+    def run(self):
+        for L in self.launches:
+            L.fn()
+
+    @property
+    def flops(self):
+        return sum(L.flops for L in self.launches)
+
+    @property
+    def quant_bytes(self):
+        return sum(L.bytes for L in self.launches)
+
+
+def sr_seed_of(recipe, name):
+    """The stochastic-rounding seed LlamaBlockStep gives tensor `name`."""
+    names = sorted(set(LLAMA_INPUT_OF.values())) + ["w_" + n for n in LLAMA_LINEARS] + \
+        ["dy_" + n for n in LLAMA_LINEARS]
+    return recipe.sr_seed_base + names.index(name)
