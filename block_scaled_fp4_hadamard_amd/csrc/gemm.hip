@@ -62,119 +62,103 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <int GRID, int OUT>
-__global__ void __launch_bounds__(kGemmThreads, 1)
-gemm_kernel(const GemmParams p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kBKBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kBKBytes];
-  __shared__ uint32_t sSA[kBM], sSB[kBN];
+// Tile order: workgroup ids are dealt round-robin to the 8 XCDs.  Groups of
+// 4 (M) x 8 (N) tiles are dealt to XCDs group by group, so the 32 workgroups
+// an XCD runs at once share 4 A strips and 8 B strips in that XCD's L2.
+constexpr int kGroupM = 4, kGroupN = 8, kXcds = 8;
 
-  // tile order: consecutive workgroups walk down M within a column band of N
-  const int tile = blockIdx.x;
-  const int bm = tile % tiles_m, bn = tile / tiles_m;
-  const int64_t m0 = (int64_t)bm * kBM, n0 = (int64_t)bn * kBN;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int64_t kbytes = p.K / 2, kblocks = p.K / 32;
-  const int nk = (int)((p.K + 127) / 128);
 
-  // global -> register staging: 4 x 16 B of A and of B, one scale dword each
-  uint4 ra[4], rb[4];
-  uint32_t rsa, rsb;
-  auto gload = [&](int kt) {
-    const int64_t kb0 = (int64_t)kt * kBKBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (t >> 2) + 64 * i, pc = t & 3;
-      const int64_t kb = kb0 + pc * 16;
-      const int64_t ga = m0 + r, gb = n0 + r;
-      ra[i] = (ga < p.M && kb < kbytes) ? *(const uint4*)(p.a_codes + ga * p.lda_codes + kb) : uint4{0u, 0u, 0u, 0u};
-      rb[i] = (gb < p.N && kb < kbytes) ? *(const uint4*)(p.b_codes + gb * p.ldb_codes + kb) : uint4{0u, 0u, 0u, 0u};
-    }
-    rsa = 0u;
-    rsb = 0u;
-    const int64_t ga = m0 + t, gb = n0 + t;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t kblk = (int64_t)kt * 4 + b;
-      if (kblk < kblocks) {
-        if (ga < p.M) rsa |= (uint32_t)p.a_scales[ga * p.lda_scales + kblk] << (8 * b);
-        if (gb < p.N) rsb |= (uint32_t)p.b_scales[gb * p.ldb_scales + kblk] << (8 * b);
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (t >> 2) + 64 * i, pc = t & 3;
-      *(uint4*)(sA + r * kBKBytes + swz(r, pc)) = ra[i];
-      *(uint4*)(sB + r * kBKBytes + swz(r, pc)) = rb[i];
-    }
-    sSA[t] = rsa;
-    sSB[t] = rsb;
-  };
 
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+struct TileMap {
+  int tiles_m, tiles_n, groups_m, groups;
+};
 
-  gload(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (kt + 1 < nk) gload(kt + 1);
+__device__ __forceinline__ bool map_tile(const TileMap& tm, int& bm, int& bn) {
+  const int id = blockIdx.x;
+  const int xcd = id % kXcds, j = id / kXcds;
+  const int g = (j / (kGroupM * kGroupN)) * kXcds + xcd, m = j % (kGroupM * kGroupN);
+  if (g >= tm.groups) return false;
+  bm = (g % tm.groups_m) * kGroupM + m % kGroupM;
+  bn = (g / tm.groups_m) * kGroupN + m / kGroupM;
+  return bm < tm.tiles_m && bn < tm.tiles_n;
+}
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Fragments of one K step from an LDS stage and its MFMAs: the wave owns
+// MT x NT 32x32 tiles at rows r0 + 32i, columns c0 + 32j of the block.
+template <int GRID, int MT, int NT>
+__device__ __forceinline__ void mma_step(const uint8_t* a, const uint8_t* b, const uint32_t* sa_w,
+                                         const uint32_t* sb_w, int r0, int c0, int lane, v16f (&acc)[MT][NT]) {
+  const int half = lane >> 5, lrow = lane & 31;
+  v8i fa[2][MT], fb[2][NT];
+  int sa[MT], sb[NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int ar = r0 + i * 32 + lrow;
+    sa[i] = (int)(sa_w[ar] >> (8 * half));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      v8i fa[4], fb[4];
-      int sa[4], sb[4];
-      const int pc = 2 * h + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_row = wm * 128 + i * 32 + (lane & 31);
-        const int rb_row = wn * 128 + i * 32 + (lane & 31);
-        const uint4 va = *(const uint4*)(sA + ra_row * kBKBytes + swz(ra_row, pc));
-        const uint4 vb = *(const uint4*)(sB + rb_row * kBKBytes + swz(rb_row, pc));
-        if constexpr (GRID == MX_GRID_E2M1) {
-          fa[i] = v8i{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-          fb[i] = v8i{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-        } else {
-          uint32_t o6[6];
-          e1m2_to_e2m3({va.x, va.y, va.z, va.w}, o6);
-          fa[i] = v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
-          e1m2_to_e2m3({vb.x, vb.y, vb.z, vb.w}, o6);
-          fb[i] = v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
-        }
-        sa[i] = (int)(sSA[ra_row] >> (8 * (lane >> 5)));
-        sb[i] = (int)(sSB[rb_row] >> (8 * (lane >> 5)));
+      const uint4 x = *(const uint4*)(a + ar * kBKBytes + swz(ar, 2 * h + half));
+      if constexpr (GRID == MX_GRID_E2M1) {
+        fa[h][i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      } else {
+        uint32_t o6[6];
+        e1m2_to_e2m3({x.x, x.y, x.z, x.w}, o6);
+        fa[h][i] = v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
       }
-      constexpr int kFmt = GRID == MX_GRID_E2M1 ? 4 : 2;   // 4: fp4 E2M1, 2: fp6 E2M3
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (h == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], kFmt, kFmt, 0, sa[i], 0, sb[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], kFmt, kFmt, 2, sa[i], 2, sb[j]);
-        }
     }
   }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int br = c0 + j * 32 + lrow;
+    sb[j] = (int)(sb_w[br] >> (8 * half));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 y = *(const uint4*)(b + br * kBKBytes + swz(br, 2 * h + half));
+      if constexpr (GRID == MX_GRID_E2M1) {
+        fb[h][j] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+      } else {
+        uint32_t o6[6];
+        e1m2_to_e2m3({y.x, y.y, y.z, y.w}, o6);
+        fb[h][j] = v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
+      }
+    }
+  }
+  constexpr int kFmt = GRID == MX_GRID_E2M1 ? 4 : 2;   // 4: fp4 E2M1, 2: fp6 E2M3
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], acc[i][j], kFmt, kFmt, 0,
+                                                                  sa[i], 0, sb[j]);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], acc[i][j], kFmt, kFmt, 2,
+                                                                  sa[i], 2, sb[j]);
+}
 
-  // epilogue
+// register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 tile;
+// for each r the 64 lanes write two 32-element row segments
+template <int OUT, bool CHECK, int MT, int NT>
+__device__ __forceinline__ void store_tile(const GemmParams& p, int64_t row0, int64_t col0, int lane,
+                                           const v16f (&acc)[MT][NT]) {
+  const int half = lane >> 5, lrow = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NT; ++j) {
+      const int64_t col = col0 + j * 32 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        if (row < p.M && col < p.N) {
+        const int64_t row = row0 + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+        if (!CHECK || (row < p.M && col < p.N)) {
           if constexpr (OUT == MX_OUT_F32)
             ((float*)p.c)[row * p.ldc + col] = acc[i][j][r];
           else
@@ -184,19 +168,349 @@ gemm_kernel(const GemmParams p, int tiles_m, int tiles_n) {
     }
 }
 
-hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s) {
-  const int tiles_m = (int)((p.M + kBM - 1) / kBM), tiles_n = (int)((p.N + kBN - 1) / kBN);
-  const dim3 g((unsigned)(tiles_m * tiles_n));
-  if (grid_kind == MX_GRID_E2M1) {
-    if (out_kind == MX_OUT_F32)
-      hipLaunchKernelGGL((gemm_kernel<MX_GRID_E2M1, MX_OUT_F32>), g, dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n);
-    else
-      hipLaunchKernelGGL((gemm_kernel<MX_GRID_E2M1, MX_OUT_BF16>), g, dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n);
+// Global -> LDS DMA of 16 (or 4) bytes per lane: LDS address = M0 + size*lane.
+// Issued as inline asm so the compiler does not place its own conservative
+// vmcnt waits for them; the kernel waits explicitly.  The instruction writes
+// no VGPR and its address operand is read at issue.  An SALU write of M0
+// needs one wait state before an LDS-DMA instruction reads it: the s_nop.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4_off(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+// a pointer that is the same in every lane, moved to SGPRs
+__device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---------------------------------------------------------------------------
+// Whole-tile path.  A 512-lane workgroup (8 waves: 2 along M x 4 along N, each
+// 128 x 64 = 4 x 2 MFMA tiles, two waves per SIMD) owns a 256 x 256 block of C.
+// K advances 256 per step: every row contributes one whole 128-byte line per
+// step, moved global -> LDS by DMA (global_load_lds_dwordx4) into one of two
+// 68 KB stages while the MFMAs consume the other.  Within a step the four
+// 64-deep K quarters are software pipelined: the fragments of quarter q+1 are
+// read from LDS while the MFMAs of quarter q run (two fragment register sets),
+// and the barrier of the next step sits behind the last quarter's MFMAs.
+constexpr int kFullThreads = 512;
+constexpr int kRowBytes = 128;            // 256 fp4 elements per row per K step
+constexpr int kFullStageBytes = kBM * kRowBytes;
+
+__device__ __forceinline__ int swz8(int row, int piece) {  // 16-byte slot within a 128-byte row
+  return (piece ^ ((row >> 1) & 7)) * 16;
+}
+
+struct Frags {
+  uint4 a[4], b[2];    // raw 16-byte code pieces (32 elements each)
+  uint32_t sa[4], sb[2];   // raw scale dwords (4 blocks); the lane's byte is picked at the MFMA
+};
+
+// fragments of K quarter q (64 deep) for the wave's 4 x 2 tiles.  Tile rows
+// start at multiples of 32, so a lane's swizzled slot depends only on its row
+// within the tile: one per-lane offset per quarter, the tiles are immediates.
+__device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const uint8_t* b, const uint32_t* sa,
+                                             const uint32_t* sb, int q, int r0, int c0, int lane) {
+  const int half = lane >> 5, lrow = lane & 31;
+  const int off = lrow * kRowBytes + swz8(lrow, 2 * q + half);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.a[i] = *(const uint4*)(a + (r0 + 32 * i) * kRowBytes + off);
+    f.sa[i] = sa[(q >> 1) * kBM + r0 + 32 * i + lrow];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f.b[j] = *(const uint4*)(b + (c0 + 32 * j) * kRowBytes + off);
+    f.sb[j] = sb[(q >> 1) * kBN + c0 + 32 * j + lrow];
+  }
+}
+
+template <int GRID>
+__device__ __forceinline__ v8i operand(const uint4& x) {
+  if constexpr (GRID == MX_GRID_E2M1) {
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
   } else {
-    if (out_kind == MX_OUT_F32)
-      hipLaunchKernelGGL((gemm_kernel<MX_GRID_E1M2, MX_OUT_F32>), g, dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n);
-    else
-      hipLaunchKernelGGL((gemm_kernel<MX_GRID_E1M2, MX_OUT_BF16>), g, dim3(kGemmThreads), 0, s, p, tiles_m, tiles_n);
+    uint32_t o6[6];
+    e1m2_to_e2m3({x.x, x.y, x.z, x.w}, o6);
+    return v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
+  }
+}
+
+// the 8 MFMAs of one quarter; OPSEL picks the scale byte pair (quarters 0,2 -> 0; 1,3 -> 2)
+// Lanes 32-63 hold the odd 32-block of each 64-deep quarter: their scale is
+// one byte above the even block's, so their dwords are shifted by 8.
+template <int GRID, int OPSEL>
+__device__ __forceinline__ void mfma_quarter(const Frags& f, v16f (&acc)[4][2], int shift) {
+  constexpr int kFmt = GRID == MX_GRID_E2M1 ? 4 : 2;   // 4: fp4 E2M1, 2: fp6 E2M3
+  const v8i b0 = operand<GRID>(f.b[0]), b1 = operand<GRID>(f.b[1]);
+  const int sb0 = (int)(f.sb[0] >> shift), sb1 = (int)(f.sb[1] >> shift);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v8i ai = operand<GRID>(f.a[i]);
+    const int sai = (int)(f.sa[i] >> shift);
+    acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, b0, acc[i][0], kFmt, kFmt, OPSEL, sai, OPSEL, sb0);
+    acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, b1, acc[i][1], kFmt, kFmt, OPSEL, sai, OPSEL, sb1);
+  }
+  // the MFMAs are side-effect free; an empty volatile asm on their results keeps
+  // them at this point of the pipeline instead of being sunk past later phases
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]));
+}
+
+// Persistent: one workgroup per CU walks its tiles (round r of the XCD-grouped
+// order: group r*8 + xcd, member = this workgroup's index on its XCD) as one
+// continuous stream of K steps, so the DMA lookahead runs across tile
+// boundaries and a tile's stores drain while the next tile computes.
+struct Walk {
+  int xcd, member, rounds;
+};
+
+__device__ __forceinline__ bool round_tile(const TileMap& tm, const Walk& w, int r, int& bm, int& bn) {
+  const int g = r * kXcds + w.xcd;
+  if (g >= tm.groups) return false;
+  bm = (g % tm.groups_m) * kGroupM + w.member % kGroupM;
+  bn = (g / tm.groups_m) * kGroupN + w.member / kGroupM;
+  return bm < tm.tiles_m && bn < tm.tiles_n;
+}
+
+// first round >= r holding a tile for this workgroup, or w.rounds
+__device__ __forceinline__ int next_round(const TileMap& tm, const Walk& w, int r, int& bm, int& bn) {
+  for (; r < w.rounds; ++r)
+    if (round_tile(tm, w, r, bm, bn)) return r;
+  return w.rounds;
+}
+
+template <int GRID, int OUT>
+__global__ void __launch_bounds__(kFullThreads, 1)
+gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kFullStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kFullStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint32_t sSA[2][2 * kBM];    // [dword d][row]: blocks 4d..4d+3
+  __shared__ __attribute__((aligned(1024))) uint32_t sSB[2][2 * kBN];
+
+  Walk w;
+  w.xcd = blockIdx.x % kXcds;
+  w.member = blockIdx.x / kXcds;
+  w.rounds = rounds;
+  int bm, bn;
+  int r = next_round(tm, w, 0, bm, bn);
+  if (r >= w.rounds) return;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r0 = wm * 128, c0 = wn * 64;
+  const int nk = (int)(p.K / 256);
+
+  // DMA: one instruction moves 64 lanes x 16 B = 1 KB = 8 rows of 128 B; wave w
+  // covers rows 32w .. 32w+31 in 4 instructions; lane i -> row +i/8, LDS slot
+  // i%8, which must hold global piece (i%8) ^ ((row>>1)&7).  Offsets are from
+  // the tile's first row (operands are < 4 GiB).
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int row = 32 * wave + 8 * c + (lane >> 3);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    oa[c] = (uint32_t)(row * p.lda_codes + piece * 16);
+    ob[c] = (uint32_t)(row * p.ldb_codes + piece * 16);
+  }
+  // scales: 8 bytes per row per step as two dwords; waves 0-3 carry A (rows
+  // 64(w&3) + lane), waves 4-7 carry B
+  const int srow = 64 * (wave & 3) + lane;
+  const bool s_is_a = wave < 4;
+  const uint32_t os = (uint32_t)(srow * (s_is_a ? p.lda_scales : p.ldb_scales));
+  const uint32_t lA = lds_addr(&sA[0][32 * wave * kRowBytes]), lB = lds_addr(&sB[0][32 * wave * kRowBytes]);
+  const uint32_t lS = s_is_a ? lds_addr(&sSA[0][64 * (wave & 3)]) : lds_addr(&sSB[0][64 * (wave & 3)]);
+
+  // DMA of K step kt of tile (tbm, tbn) into stage st
+  auto issue = [&](int tbm, int tbn, int kt, int st) {
+    const int64_t m0 = (int64_t)tbm * kBM, n0 = (int64_t)tbn * kBN;
+    const uint8_t* abase = wave_uniform(p.a_codes + m0 * p.lda_codes);
+    const uint8_t* bbase = wave_uniform(p.b_codes + n0 * p.ldb_codes);
+    const uint8_t* sbase = wave_uniform(s_is_a ? p.a_scales + m0 * p.lda_scales : p.b_scales + n0 * p.ldb_scales);
+    const uint32_t kb = (uint32_t)kt * kRowBytes;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      dma16_off(abase, oa[c] + kb, lA + st * kFullStageBytes + c * 8 * kRowBytes);
+      dma16_off(bbase, ob[c] + kb, lB + st * kFullStageBytes + c * 8 * kRowBytes);
+    }
+    dma4_off(sbase, os + 8 * kt, lS + st * (2 * kBM * 4));
+    dma4_off(sbase, os + 8 * kt + 4, lS + st * (2 * kBM * 4) + kBM * 4);
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // the tile after the current one, and the DMA cursor two K steps ahead
+  int nbm = 0, nbn = 0;
+  int rn = next_round(tm, w, r + 1, nbm, nbn);
+  Frags f0, f1;
+  const int shift = 8 * (lane >> 5);
+  issue(bm, bn, 0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_barrier();
+  if (nk > 1) issue(bm, bn, 1, 1);
+  else if (rn < w.rounds) issue(nbm, nbn, 0, 1);
+  load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane);
+  int st = 0;
+  for (;;) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint8_t* a = sA[st];
+      const uint8_t* b = sB[st];
+      const uint32_t* sa = sSA[st];
+      const uint32_t* sb = sSB[st];
+      // sched_barrier keeps each phase where it is written: without it the
+      // scheduler hoists every quarter's reads to the top and runs out of VGPRs
+      load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_quarter<GRID, 0>(f0, acc, shift);
+      __builtin_amdgcn_sched_barrier(0);
+      load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_quarter<GRID, 2>(f1, acc, shift);
+      __builtin_amdgcn_sched_barrier(0);
+      load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_quarter<GRID, 0>(f0, acc, shift);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool more = kt + 1 < nk || rn < w.rounds;
+      if (more) {
+        // the next step's stage has landed for this wave; every wave has read
+        // its last fragments of this stage; then refill it two steps ahead
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        if (kt + 2 < nk) issue(bm, bn, kt + 2, st);
+        else if (rn < w.rounds && kt + 2 - nk < nk) issue(nbm, nbn, kt + 2 - nk, st);
+        st ^= 1;
+        load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_quarter<GRID, 2>(f1, acc, shift);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    store_tile<OUT, false, 4, 2>(p, (int64_t)bm * kBM + r0, (int64_t)bn * kBN + c0, lane, acc);
+    if (rn >= w.rounds) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    r = rn;
+    bm = nbm;
+    bn = nbn;
+    rn = next_round(tm, w, r + 1, nbm, nbn);
+  }
+}
+
+// Any shape (ragged M, N; K % 32 == 0): bounds-checked loads through registers.
+template <int GRID, int OUT>
+__global__ void __launch_bounds__(kGemmThreads, 1)
+gemm_general_kernel(const GemmParams p, const TileMap tm) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kBKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kBKBytes];
+  __shared__ uint32_t sSA[kBM], sSB[kBN];
+
+  int bm, bn;
+  if (!map_tile(tm, bm, bn)) return;
+  const int64_t m0 = (int64_t)bm * kBM, n0 = (int64_t)bn * kBN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t kbytes = p.K / 2, kblocks = p.K / 32;
+  const int nk = (int)((p.K + 127) / 128);
+  const int pc = t & 3;
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int64_t kb = (int64_t)kt * kBKBytes + pc * 16;
+    uint4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (t >> 2) + 64 * i;
+      ra[i] = (m0 + r < p.M && kb < kbytes) ? *(const uint4*)(p.a_codes + (m0 + r) * p.lda_codes + kb)
+                                             : uint4{0u, 0u, 0u, 0u};
+      rb[i] = (n0 + r < p.N && kb < kbytes) ? *(const uint4*)(p.b_codes + (n0 + r) * p.ldb_codes + kb)
+                                             : uint4{0u, 0u, 0u, 0u};
+    }
+    uint32_t xa = 0u, xb = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t kblk = (int64_t)kt * 4 + b;
+      if (kblk < kblocks) {
+        if (m0 + t < p.M) xa |= (uint32_t)p.a_scales[(m0 + t) * p.lda_scales + kblk] << (8 * b);
+        if (n0 + t < p.N) xb |= (uint32_t)p.b_scales[(n0 + t) * p.ldb_scales + kblk] << (8 * b);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (t >> 2) + 64 * i;
+      *(uint4*)(&sA[r * kBKBytes + swz(r, pc)]) = ra[i];
+      *(uint4*)(&sB[r * kBKBytes + swz(r, pc)]) = rb[i];
+    }
+    sSA[t] = xa;
+    sSB[t] = xb;
+    __syncthreads();
+    mma_step<GRID, 4, 4>(sA, sB, sSA, sSB, wm * 128, wn * 128, lane, acc);
+  }
+  store_tile<OUT, true, 4, 4>(p, m0 + wm * 128, n0 + wn * 128, lane, acc);
+}
+
+template <int GRID, int OUT>
+static void launch_kind(const GemmParams& p, const TileMap& tm, bool full, dim3 g, hipStream_t s) {
+  if (full) {
+    // one workgroup per CU: 8 XCDs x 32 members; round r deals group r*8+xcd
+    const int rounds = (tm.groups + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT>), dim3(kXcds * kGroupM * kGroupN), dim3(kFullThreads), 0, s, p,
+                       tm, rounds);
+  } else {
+    hipLaunchKernelGGL((gemm_general_kernel<GRID, OUT>), g, dim3(kGemmThreads), 0, s, p, tm);
+  }
+}
+
+hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s) {
+  TileMap tm;
+  tm.tiles_m = (int)((p.M + kBM - 1) / kBM);
+  tm.tiles_n = (int)((p.N + kBN - 1) / kBN);
+  tm.groups_m = (tm.tiles_m + kGroupM - 1) / kGroupM;
+  const int groups_n = (tm.tiles_n + kGroupN - 1) / kGroupN;
+  tm.groups = tm.groups_m * groups_n;
+  const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
+  const dim3 g((unsigned)wgs);
+  // the DMA path needs whole tiles, whole 256-element K steps (at least two) and
+  // 4-byte aligned scale rows
+  const bool full = (p.M % kBM == 0) && (p.N % kBN == 0) && (p.K % 256 == 0) && (p.K >= 512) &&
+                    ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.b_scales % 4 == 0) &&
+                    (p.lda_scales % 4 == 0) && (p.ldb_scales % 4 == 0);
+  if (grid_kind == MX_GRID_E2M1) {
+    if (out_kind == MX_OUT_F32) launch_kind<MX_GRID_E2M1, MX_OUT_F32>(p, tm, full, g, s);
+    else launch_kind<MX_GRID_E2M1, MX_OUT_BF16>(p, tm, full, g, s);
+  } else {
+    if (out_kind == MX_OUT_F32) launch_kind<MX_GRID_E1M2, MX_OUT_F32>(p, tm, full, g, s);
+    else launch_kind<MX_GRID_E1M2, MX_OUT_BF16>(p, tm, full, g, s);
   }
   return hipGetLastError();
 }

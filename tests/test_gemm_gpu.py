@@ -28,7 +28,8 @@ def run_gemm(a, b, grid, out_dtype=torch.float32):
 
 @pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
 @pytest.mark.parametrize("m,n,k", [(256, 256, 256), (300, 200, 160), (513, 257, 1088), (32, 32, 32),
-                                   (1, 7, 64), (640, 520, 4096)])
+                                   (1, 7, 64), (640, 520, 4096), (512, 768, 1024), (256, 512, 384),
+                                   (768, 256, 640)])
 def test_gemm_random_operands(grid, m, n, k):
     announce("gemm random %s %dx%dx%d" % (grid, m, n, k))
     rng = np.random.default_rng(m * 7 + n * 3 + k)
