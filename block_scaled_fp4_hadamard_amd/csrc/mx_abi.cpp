@@ -52,7 +52,7 @@ mx_status quantize_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
   const bool do_row = (axis & MX_AXIS_ROW) != 0, do_col = (axis & MX_AXIS_COL) != 0;
   if (rows == 0 || cols == 0) return MX_OK;
   if (x == nullptr || !aligned16(x)) return MX_ERR_INVALID;
-  if (ld_x < cols || ld_x % 8 != 0 || cols % 8 != 0) return MX_ERR_INVALID;
+  if (ld_x < cols || ld_x % 8 != 0 || cols % 8 != 0 || ld_x >= (int64_t(1) << 25)) return MX_ERR_INVALID;
   if (do_row) {
     if (cols % block != 0) return MX_ERR_INVALID;
     mx_status s = check_qtensor(row_out, rows, cols, block);

@@ -122,19 +122,22 @@ __device__ __forceinline__ float rn32_from_limbs(int64_t (&acc)[9]) {
   return __uint_as_float(sbit | ((uint32_t)(e + 127) << 23) | (mant & 0x7FFFFFu));
 }
 
-// Exact S_i for output i of a chunk of N bf16 values (bit patterns in xb[]),
-// with sign vector mask (bit j set: x_j negated).  All inputs finite.
-template <int N>
-__device__ __forceinline__ float exact_hadamard_rn32(const uint32_t (&xb)[N], int i, uint32_t mask) {
+// Exact S_i for output i of a chunk of N bf16 values, input j's bit pattern
+// given by get(j), with sign vector mask (bit j set: x_j negated).  Sets
+// `nonfinite` when an input is Inf or NaN (the sum is then meaningless).
+template <int N, typename Get>
+__device__ __forceinline__ float exact_hadamard_rn32(Get get, int i, uint32_t mask, bool& nonfinite) {
   int64_t acc[9];
 #pragma unroll
   for (int l = 0; l < 9; ++l) acc[l] = 0;
+  nonfinite = false;
 #pragma unroll 1
   for (int j = 0; j < N; ++j) {
-    const uint32_t b = xb[j];
+    const uint32_t b = get(j);
     const uint32_t ef = (b >> 7) & 0xFFu;
+    nonfinite |= ef == 0xFFu;
     const uint32_t sig = ef ? ((b & 0x7Fu) | 0x80u) : (b & 0x7Fu);
-    if (sig == 0u) continue;
+    if (sig == 0u || ef == 0xFFu) continue;
     const int p = (int)(ef ? ef : 1u) - 1;                 // 0 .. 253
     const int L = p >> 5, off = p & 31;
     const uint64_t v = (uint64_t)sig << off;

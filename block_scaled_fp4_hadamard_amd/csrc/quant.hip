@@ -1,155 +1,185 @@
 // Fused block-Hadamard + block-absmax + 4-bit cast for gfx950 (MI355X).
 //
-// One workgroup (256 lanes) owns a 32-row x 256-column bf16 tile:
-//   1. coalesced 16-byte loads of the tile (each row segment is 512 contiguous
-//      bytes), widened to fp32 once and staged in LDS (padded chunks so both
-//      the row-chunk reads and the column reads are bank-conflict free);
-//      the same pass takes a tile-wide max / min-nonzero of |x| that decides
-//      whether float64 butterflies are exact for every chunk of the tile;
-//   2. row pass: lane (r, k) rotates, scales and casts the 32-element chunk k
-//      of row r and writes 16 code bytes + 1 scale byte;
-//   3. column pass: lane c does the same for column c over the tile's 32 rows
-//      (the Wgrad operand, blocked along tokens) and writes the transposed
-//      output.
-// The rotation (deterministic H16/H32 or random-sign RHT, "Pre-addestramento
-// ... con MXFP4", Metodologia) runs as an in-register Walsh-Hadamard
-// butterfly in float64: with the tile's inputs spanning <= 40 binades every
-// partial sum is exact, so y = RN32(RN32(S) * c) matches the exact-sum
-// definition bit for bit.  Tiles outside that (wide spans, Inf/NaN, values near
-// the top of the range) take an exact fixed-point path instead.
+// A persistent workgroup (256 lanes, 4 waves) walks 32-row x 256-column bf16
+// tiles.  Per tile:
+//   1. the tile's 16-byte row pieces, loaded into registers while the
+//      previous tile was being cast, give a tile-wide max and min-nonzero of
+//      |x| (packed 16-bit integer ops); one barrier combines the waves;
+//   2. the tile is staged in LDS as bf16 (XOR-swizzled 16-byte pieces: the
+//      staging writes, the row-chunk reads and the column reads are all free
+//      of bank conflicts), and the next tile's loads are issued;
+//   3. row pass (blocks of 32 along a row: the Fprop/Dgrad operand) and
+//      column pass (blocks of 32 down a column: the Wgrad operand, written
+//      transposed).
+//
+// The rotation of a 32-element block (deterministic H16/H32 or random-sign
+// RHT, "Pre-addestramento ... con MXFP4", Metodologia) is defined as
+// y = RN32(RN32(S) * c) with S the exact signed sum.  The hot path computes S
+// as a matrix product on the matrix cores: D = A . B with A the 32x32
+// sign-Hadamard matrix (rows permuted so that each lane's 16 results are 16
+// consecutive outputs of one block) and B = 32 blocks of inputs, one
+// v_mfma_f32_32x32x16_bf16 per 16 inputs.  Products of bf16 inputs with +-1
+// are exact, and every partial sum of a block is an integer multiple of its
+// smallest input's ulp; when the inputs span at most 11 binades every such
+// sum fits fp32's 24-bit significand, so the fp32 accumulation is exact.
+// Tiles spanning 12..23 binades are split by magnitude into a high part
+// (within 11 binades of the tile maximum) and a low part, each product exact,
+// and RN32(S_hi + S_lo) = RN32(S) takes one fp32 add.  Wider tiles (and tiles
+// with values below 2^-119, whose partial sums could be subnormal) take
+// float64 butterflies, exact up to a 40-binade span; non-finite,
+// near-overflow and wider tiles take an exact fixed-point path.
+//
 // The E2M1 round-to-nearest-even cast uses gfx950's scaled fp4 conversion
 // (ties to even, saturating, dividing by the power-of-two scale given as a
 // float); stochastic rounding and the uniform grid run in plain VALU code.
+//
+// Tile order is XCD-aware: workgroup w runs on XCD w % 8, and the 8 row tiles
+// of a 256x256 region are all taken by workgroups of one XCD at about the
+// same time, so the column-wise output's pieces of one 128-byte line meet in
+// that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <algorithm>
 #include "mx_device.h"
 #include "mx_kernels.h"
 
 namespace mx {
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short ss2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileRows = 32;
 constexpr int kTileCols = 256;
 constexpr int kThreads = 256;
-constexpr int kChunkPitch = 36;                    // floats per 32-float chunk in LDS (+16 B pad)
-constexpr int kRowPitch = 8 * kChunkPitch;         // floats per tile row in LDS
-constexpr int kGroup = 8;                          // row tiles sharing one XCD (a 256x256 region)
+constexpr int kRowBytes = 2 * kTileCols;           // one tile row of bf16 in LDS
+constexpr int kPartBytes = kTileRows * kRowBytes;  // one staged copy of the tile (16 KB)
+constexpr int kGroup = 8;                          // row tiles of one region (256 rows)
+constexpr int kWgPerCu = 4;                        // resident workgroups per CU in the persistent grid
 
 // fp32 RN32(1/sqrt(32)) = sqrt(2)/8 and 1/sqrt(16)
 constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;
 constexpr float kInvSqrt16 = 0.25f;
+
+// tile classes (uniform per tile)
+constexpr int kClsMfma1 = 0;     // matrix-core sums, one part (or no rotation)
+constexpr int kClsMfma2 = 1;     // matrix-core sums, high + low parts
+constexpr int kClsF64 = 2;       // float64 butterflies
+constexpr int kClsSpecial = 3;   // exact fixed point, careful casting
 
 __device__ __forceinline__ uint32_t e8m0_scale_bits(uint32_t byte) {
   // the float whose exponent the scaled conversions divide by: 2^(byte-127)
   return byte ? (byte << 23) : 0x00400000u;        // 2^-127 is a subnormal float
 }
 
-// Cast one 32-element block y[] (E2M1 or E1M2, RTNE or SR) into 4 code
-// dwords; returns the scale byte.  `careful` blocks may hold non-finite y.
+// LDS byte offset of tile element (r, c): 16-byte piece p = c / 8 of row r is
+// stored at piece p ^ s(r, p); s flips piece bit 1 for the right half of a
+// row, bit 0 for odd rows and bit 2 for rows 8..15 and 24..31.  Since s
+// depends on r only through bits 0 and 3, lds_col(c, r & 9) + r * kRowBytes
+// addresses any row r: the passes keep a few such per-lane bases and index
+// rows with immediate offsets.
+__device__ __forceinline__ uint32_t lds_col(int c, int rbits) {
+  const int p = c >> 3;
+  const int s = (((p >> 4) & 1) << 1) | (rbits & 1) | (((rbits >> 3) & 1) << 2);
+  return (uint32_t)(((p ^ s) << 4) + ((c & 7) << 1));
+}
+__device__ __forceinline__ uint32_t lds_off(int r, int c) { return (uint32_t)(r * kRowBytes) + lds_col(c, r & 9); }
+
+// 4-bit code of one value y of a block with scale byte `byte` (finite y):
+// sign bit 3, magnitude code = |y| / 2^(byte-127) on the grid, rounded by
+// RTNE or (SR) up iff the random word u is below floor(frac * 2^32).
 template <int GRID, int ROUND>
-__device__ __forceinline__ uint32_t cast_block(const float (&y)[32], bool careful, const uint32_t (&u)[32],
-                                               uint32_t (&w)[4]) {
-  constexpr int kEmax = GRID == MX_GRID_E2M1 ? 2 : 0;
-  uint32_t expf;
-  bool nonfinite = false;
-  if (!careful) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(y[i]));
-    expf = __float_as_uint(m) >> 23;
+__device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u) {
+  const int ebias = (int)byte - 127;
+  uint32_t k;
+  if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
+    k = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yy, 0.0f, __uint_as_float(e8m0_scale_bits(byte)), 0) & 0xFu;
+    return k;
+  } else if constexpr (GRID == MX_GRID_E2M1) {
+    // Stochastic rounding in plain arithmetic.  v = |y| / 2^e (exact unless
+    // v < 2^-126, where P below is 0 either way); the quantum q is 1/2 on
+    // [0,2), 1 on [2,4), 2 on [4,8); t = v / q, lo = floor(t) and
+    // P = floor((t - lo) * 2^32) (t - lo is exact); round up iff u < P.  The
+    // magnitude code of lo is floor(t) + 2*log2(q) + 2 on every piece.
+    // (gfx950's stochastic fp4 conversion is not used: it draws only 22 of
+    // the 32 random bits, a coarser rule than this one.)
+    const float v = ldexpf(fabsf(yy), -ebias);
+    const int qexp = max((int)(__float_as_uint(v) >> 23) - 128, -1);
+    const float t = ldexpf(v, -qexp);
+    const float fl = floorf(t);
+    const uint32_t pr = (uint32_t)ldexpf(t - fl, 32);
+    k = (uint32_t)fl + (uint32_t)(2 * qexp + 2) + (u < pr ? 1u : 0u);
   } else {
-    uint32_t mb = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mb = max(mb, __float_as_uint(y[i]) & 0x7FFFFFFFu);
-    nonfinite = mb >= 0x7F800000u;
-    expf = mb >> 23;
-  }
-  const uint32_t byte = expf > (uint32_t)kEmax ? expf - kEmax : 0u;
-  if (nonfinite) {
-    w[0] = w[1] = w[2] = w[3] = 0u;
-    return 0xFFu;
-  }
-  if constexpr (GRID == MX_GRID_E2M1) {
-    const float sc = __uint_as_float(e8m0_scale_bits(byte));
+    // uniform grid: magnitude code = |y| * 2^(2-e), rounded
+    const float t = ldexpf(fabsf(yy), 2 - ebias);
     if constexpr (ROUND == MX_ROUND_RTNE) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t r = 0;
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 0], y[8 * d + 1], sc, 0);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 2], y[8 * d + 3], sc, 1);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 4], y[8 * d + 5], sc, 2);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 6], y[8 * d + 7], sc, 3);
-        w[d] = r;
-      }
+      k = (uint32_t)rintf(t);
     } else {
-      // Stochastic rounding in plain arithmetic.  v = |y| / 2^e (exact unless
-      // v < 2^-126, where P below is 0 either way); the quantum q is 1/2 on
-      // [0,2), 1 on [2,4), 2 on [4,8); t = v / q, lo = floor(t) and
-      // P = floor((t - lo) * 2^32) (t - lo is exact); round up iff u < P.
-      // The magnitude code of lo is floor(t) + 2*log2(q) + 2 on every piece.
-      // (gfx950's stochastic fp4 conversion is not used: it draws only 22 of
-      // the 32 random bits, a coarser rule than this one.)
-      const int ebias = (int)byte - 127;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t r = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float yy = y[8 * d + q];
-          const float v = ldexpf(fabsf(yy), -ebias);
-          const int qexp = max((int)(__float_as_uint(v) >> 23) - 128, -1);
-          const float t = ldexpf(v, -qexp);
-          const float fl = floorf(t);
-          const uint32_t pr = (uint32_t)ldexpf(t - fl, 32);
-          uint32_t k = (uint32_t)fl + (uint32_t)(2 * qexp + 2) + (u[8 * d + q] < pr ? 1u : 0u);
-          k = min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
-          r |= k << (4 * q);
-        }
-        w[d] = r;
-      }
+      const float fl = floorf(t);
+      const uint32_t pr = (uint32_t)ldexpf(t - fl, 32);       // floor(frac * 2^32)
+      k = (uint32_t)fl + (u < pr ? 1u : 0u);
     }
-  } else {
-    // uniform grid: magnitude code k = v*4 rounded, v = |y| / 2^e; t = |y| * 2^(2-e)
-    const int sh = 2 - ((int)byte - 127);
+  }
+  return min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
+}
+
+// Scale byte of a block whose largest |y| has float exponent field expf.
+template <int GRID>
+__device__ __forceinline__ uint32_t scale_byte(uint32_t expf) {
+  constexpr uint32_t kEmax = GRID == MX_GRID_E2M1 ? 2u : 0u;
+  return expf > kEmax ? expf - kEmax : 0u;
+}
+
+// Cast one 32-element block y[] of finite values into 4 code dwords; returns
+// the scale byte.  For SR, y[i] draws Philox word i % 4 of counter block
+// ctr + i / 4 (stream `stream`, key k0:k1).
+template <int GRID, int ROUND>
+__device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ctr, uint32_t stream, uint32_t k0,
+                                               uint32_t k1, uint32_t (&w)[4]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(y[i]));
+  const uint32_t byte = scale_byte<GRID>(__float_as_uint(m) >> 23);
+  if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
+    // ties-to-even, saturating: gfx950's scaled conversion, two values a time
+    const float sc = __uint_as_float(e8m0_scale_bits(byte));
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       uint32_t r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 0], y[8 * d + 1], sc, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 2], y[8 * d + 3], sc, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 4], y[8 * d + 5], sc, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 6], y[8 * d + 7], sc, 3);
+      w[d] = r;
+    }
+  } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float yy = y[8 * d + q];
-        const float t = ldexpf(fabsf(yy), sh);
-        uint32_t k;
-        if constexpr (ROUND == MX_ROUND_RTNE) {
-          k = (uint32_t)rintf(t);
-        } else {
-          const float fl = floorf(t);
-          const uint32_t p = (uint32_t)ldexpf(t - fl, 32);     // floor(frac * 2^32)
-          k = (uint32_t)fl + (u[8 * d + q] < p ? 1u : 0u);
-        }
-        k = min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
-        r |= k << (4 * q);
+    for (int d = 0; d < 4; ++d) {
+      uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      if constexpr (ROUND == MX_ROUND_SR) {
+        const uint64_t b0 = ctr + 2 * d, b1 = b0 + 1;
+        const U4 r0 = philox4x32_10((uint32_t)b0, (uint32_t)(b0 >> 32), stream, 0u, k0, k1);
+        const U4 r1 = philox4x32_10((uint32_t)b1, (uint32_t)(b1 >> 32), stream, 0u, k0, k1);
+        u[0] = r0.x; u[1] = r0.y; u[2] = r0.z; u[3] = r0.w;
+        u[4] = r1.x; u[5] = r1.y; u[6] = r1.z; u[7] = r1.w;
       }
+      uint32_t r = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r |= cast_one<GRID, ROUND>(y[8 * d + q], byte, u[q]) << (4 * q);
       w[d] = r;
     }
   }
   return byte;
 }
 
-// Rotate 32 fp32 inputs (exact bf16 values) in place along the chunk.
-template <int HAD, bool RHT>
-__device__ __forceinline__ void rotate_fast(float (&y)[32], uint32_t mask) {
-  double v[32];
+// 16-point Walsh-Hadamard butterflies (natural order) in float64.
+__device__ __forceinline__ void fwht16(double (&v)[16]) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float x = y[i];
-    if constexpr (RHT) x = __uint_as_float(__float_as_uint(x) ^ (((mask >> (i % HAD)) & 1u) << 31));
-    v[i] = (double)x;
-  }
+  for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
-  for (int h = 1; h < HAD; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
       if ((i & h) == 0) {
         const double a = v[i], b = v[i + h];
         v[i] = a + b;
@@ -157,188 +187,565 @@ __device__ __forceinline__ void rotate_fast(float (&y)[32], uint32_t mask) {
       }
     }
   }
-  const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) y[i] = __builtin_fmaf((float)v[i], c, 0.0f);   // +0 addend: a zero sum gives +0
 }
 
-// Exact rotation for special tiles; a chunk with a non-finite input gives NaN.
+// Inputs x[0 .. 16) (chunk positions base .. base+16) as float64, with the
+// random signs applied: input j of a Hadamard chunk is negated when bit j of
+// the mask is set.
 template <int HAD>
-__device__ __noinline__ void rotate_exact(float (&y)[32], uint32_t mask) {
-  const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
-#pragma unroll 1
-  for (int base = 0; base < 32; base += HAD) {
-    uint32_t xb[HAD];
-    bool nonfinite = false;
-    for (int j = 0; j < HAD; ++j) {
-      xb[j] = __float_as_uint(y[base + j]) >> 16;
-      nonfinite |= ((xb[j] >> 7) & 0xFFu) == 0xFFu;
-    }
-#pragma unroll 1
-    for (int i = 0; i < HAD; ++i) {
-      const float s = nonfinite ? __uint_as_float(0x7FC00000u) : exact_hadamard_rn32<HAD>(xb, i, mask);
-      y[base + i] = __builtin_fmaf(s, c, 0.0f);
-    }
-  }
-}
-
-// 32 Philox words for elements [i0, i0+32) of a stream (i0 % 4 == 0).
-__device__ __forceinline__ void philox_words32(uint64_t i0, uint32_t stream, uint32_t k0, uint32_t k1,
-                                               uint32_t (&u)[32]) {
-  const uint64_t b0 = i0 >> 2;
+__device__ __forceinline__ void widen16(const float (&x)[16], int base, uint32_t mask, double (&v)[16]) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint64_t b = b0 + q;
-    const U4 r = philox4x32_10((uint32_t)b, (uint32_t)(b >> 32), stream, 0u, k0, k1);
-    u[4 * q + 0] = r.x;
-    u[4 * q + 1] = r.y;
-    u[4 * q + 2] = r.z;
-    u[4 * q + 3] = r.w;
+  for (int j = 0; j < 16; ++j)
+    v[j] = (double)__uint_as_float(__float_as_uint(x[j]) ^ (((mask >> ((base + j) % HAD)) & 1u) << 31));
+}
+
+// 32 inputs of one block, fetched 16 at a time by load16(h, x) (h = 0, 1),
+// rotated in float64 butterflies (one 32-point or two 16-point transforms):
+// y = RN32(RN32(S) * c), exact while the inputs span at most 40 binades.
+// The second half is fetched only after the first is transformed, so that
+// at most 32 float64 values are live besides the first half's results.
+// Without rotation (HAD == 0) y = x.
+template <int HAD, typename Load>
+__device__ __forceinline__ void load_rotate(Load load16, uint32_t mask, float (&y)[32]) {
+  if constexpr (HAD == 0) {
+    float x0[16], x1[16];
+    load16(0, x0);
+    load16(1, x1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      y[i] = x0[i];
+      y[16 + i] = x1[i];
+    }
+  } else {
+    const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
+    double lo[16], hi[16];
+    float x[16];
+    load16(0, x);
+    widen16<HAD>(x, 0, mask, lo);
+    fwht16(lo);
+    // pin the first half's results here (an empty asm that reads and writes
+    // them), so that the compiler cannot sink its work below the second
+    // half's loads
+    if constexpr (HAD == 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        y[i] = __builtin_fmaf((float)lo[i], c, 0.0f);   // +0 addend: a zero sum gives +0
+        asm volatile("" : "+v"(y[i]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(lo[i]));
+    }
+    asm volatile("" ::: "memory");
+    load16(1, x);
+    widen16<HAD>(x, 16, mask, hi);
+    fwht16(hi);
+    if constexpr (HAD == 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[16 + i] = __builtin_fmaf((float)hi[i], c, 0.0f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const double a = lo[i], b = hi[i];
+        y[i] = __builtin_fmaf((float)(a + b), c, 0.0f);
+        y[16 + i] = __builtin_fmaf((float)(a - b), c, 0.0f);
+      }
+    }
   }
 }
 
-template <int HAD, bool RHT, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
-__global__ void __launch_bounds__(kThreads)
-quant_tile_kernel(const QuantParams p) {
-  __shared__ __attribute__((aligned(16))) float tile[kTileRows * kRowPitch];
+// Sign-Hadamard MFMA operand A (32 x 32, two K-halves): lane l holds row
+// m = l % 32, inputs j = 16h + 8(l / 32) + e.  Row m produces output
+// o = 16((m >> 2) & 1) + 4(m >> 3) + (m & 3), which places outputs
+// 16(l / 32) .. 16(l / 32) + 15 of every block in lane l's 16 accumulators.
+// Entry: (-1)^(popcount(o & j) + sign bit j) within a Hadamard chunk, 0
+// across the two chunks of an H16 block.
+template <int HAD>
+__device__ __forceinline__ void hadamard_operand(uint32_t mask, int lane, bf16x8 (&ha)[2]) {
+  const int m = lane & 31;
+  const int o = ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 16 * h + 8 * (lane >> 5) + e;
+      const uint32_t neg = (__popc((unsigned)(o & j & (HAD - 1))) ^ (mask >> (j & (HAD - 1)))) & 1u;
+      const bool zero = HAD == 16 && ((o ^ j) & 16) != 0;
+      v[e] = zero ? (unsigned short)0 : (unsigned short)(neg ? 0xBF80u : 0x3F80u);
+    }
+    ha[h] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// Low part of two packed bf16 values: those with |x| below the threshold t
+// (bf16 magnitude bits, both halves of t2); the high part is w ^ low.
+__device__ __forceinline__ uint32_t split_low(uint32_t w, uint32_t t2) {
+  const us2 m = __builtin_bit_cast(us2, w & 0x7FFF7FFFu);
+  const ss2 d = __builtin_bit_cast(ss2, m - __builtin_bit_cast(us2, t2));
+  const ss2 below = d >> (ss2){15, 15};            // 0xFFFF where m < t
+  return w & __builtin_bit_cast(uint32_t, below);
+}
+
+// Cast one lane's half of a block: y[0..16) are outputs 16(l / 32) .. +15,
+// the other half is in lane l ^ 32.  Writes 2 code dwords; returns the scale
+// byte.  For SR, y[i] draws Philox word i % 4 of counter block ctr + i / 4.
+template <int GRID, int ROUND>
+__device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int lane, uint64_t ctr, uint32_t stream,
+                                                    uint32_t k0, uint32_t k1, uint32_t (&w)[2]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
+  const uint32_t mb = __float_as_uint(m);
+  const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+  const uint32_t other = lane < 32 ? sw[1] : sw[0];
+  const uint32_t byte = scale_byte<GRID>(max(mb, other) >> 23);
+  if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
+    const float sc = __uint_as_float(e8m0_scale_bits(byte));
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      uint32_t r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 0], y[8 * d + 1], sc, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 2], y[8 * d + 3], sc, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 4], y[8 * d + 5], sc, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 6], y[8 * d + 7], sc, 3);
+      w[d] = r;
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      if constexpr (ROUND == MX_ROUND_SR) {
+        const uint64_t b0 = ctr + 2 * d, b1 = b0 + 1;
+        const U4 r0 = philox4x32_10((uint32_t)b0, (uint32_t)(b0 >> 32), stream, 0u, k0, k1);
+        const U4 r1 = philox4x32_10((uint32_t)b1, (uint32_t)(b1 >> 32), stream, 0u, k0, k1);
+        u[0] = r0.x; u[1] = r0.y; u[2] = r0.z; u[3] = r0.w;
+        u[4] = r1.x; u[5] = r1.y; u[6] = r1.z; u[7] = r1.w;
+      }
+      uint32_t r = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r |= cast_one<GRID, ROUND>(y[8 * d + q], byte, u[q]) << (4 * q);
+      w[d] = r;
+    }
+  }
+  return byte;
+}
+
+// Row sums of 32 blocks on the matrix cores: b[h] holds the lane's inputs
+// 16h + 8(l / 32) .. +7 of block l % 32 (high part, and low part when TWO).
+template <bool TWO>
+__device__ __forceinline__ void mfma_block_sums(const bf16x8 (&ha)[2], const uint4 (&bh)[2], const uint4 (&bl)[2],
+                                                float c, float (&y)[16]) {
+  f32x16 hi = {}, lo = {};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[h], __builtin_bit_cast(bf16x8, bh[h]), hi, 0, 0, 0);
+    if constexpr (TWO) lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[h], __builtin_bit_cast(bf16x8, bl[h]), lo, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float s = TWO ? hi[r] + lo[r] : hi[r];    // both exact: one rounding, RN32(S)
+    y[r] = __builtin_fmaf(s, c, 0.0f);               // +0 addend: a zero sum gives +0
+  }
+}
+
+// Element i of a block after the rotation, computed exactly from the bf16
+// inputs get(j): y = RN32(RN32(S) * c), NaN when its Hadamard chunk holds a
+// non-finite input.  Without rotation, y = x.
+template <int HAD, typename Get>
+__device__ __forceinline__ float special_value(Get get, int i, uint32_t mask) {
+  if constexpr (HAD == 0) {
+    return __uint_as_float(get(i) << 16);
+  } else {
+    const int base = i & ~(HAD - 1);
+    bool nonfinite;
+    const float s = exact_hadamard_rn32<HAD>([&](int j) { return get(base + j); }, i & (HAD - 1), mask, nonfinite);
+    const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
+    return nonfinite ? __uint_as_float(0x7FC00000u) : __builtin_fmaf(s, c, 0.0f);
+  }
+}
+
+// One block of a tile that needs the exact rotation or careful casting
+// (non-finite, near-overflow or very wide inputs): element by element, every
+// y computed twice (once for the block maximum, once to cast), so that
+// nothing here needs private arrays.  A block with a non-finite y gets scale
+// 0xFF and zero codes.
+template <int HAD, int GRID, int ROUND, typename Get>
+__device__ __forceinline__ void special_block(Get get, uint32_t mask, uint64_t ctr, uint32_t stream, uint32_t k0,
+                                              uint32_t k1, uint8_t* codes, uint8_t* scale) {
+  uint32_t mb = 0;
+#pragma unroll 1
+  for (int i = 0; i < 32; ++i) mb = max(mb, __float_as_uint(special_value<HAD>(get, i, mask)) & 0x7FFFFFFFu);
+  if (mb >= 0x7F800000u) {
+    *(uint4*)codes = uint4{0u, 0u, 0u, 0u};
+    *scale = 0xFFu;
+    return;
+  }
+  const uint32_t byte = scale_byte<GRID>(mb >> 23);
+#pragma unroll 1
+  for (int g = 0; g < 8; ++g) {                 // 4 elements: one Philox block
+    U4 r = {0u, 0u, 0u, 0u};
+    if constexpr (ROUND == MX_ROUND_SR)
+      r = philox4x32_10((uint32_t)(ctr + g), (uint32_t)((ctr + g) >> 32), stream, 0u, k0, k1);
+    uint32_t half = 0;
+    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 0, mask), byte, r.x);
+    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 1, mask), byte, r.y) << 4;
+    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 2, mask), byte, r.z) << 8;
+    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 3, mask), byte, r.w) << 12;
+    *(uint16_t*)(codes + 2 * g) = (uint16_t)half;
+  }
+  *scale = (uint8_t)byte;
+}
+
+// Tile walk: workgroup (xcd, j) of J per XCD takes the XCD's tile sequence
+// tau = j, j + J, ...; tau / 8 is the XCD's region count, tau % 8 the row tile
+// inside the region.  Moves tau to the next tile that exists; false at the end.
+__device__ __forceinline__ bool next_tile(const QuantParams& p, uint32_t xcd, uint32_t J, uint32_t& tau,
+                                          int64_t& row0, int64_t& col0) {
+  const uint32_t n_regions = (uint32_t)p.n_col_tiles * (uint32_t)p.n_row_groups;
+  for (;; tau += J) {
+    const uint32_t region = (tau >> 3) * 8u + xcd;
+    if (region >= n_regions) return false;
+    const uint32_t col_tile = region / (uint32_t)p.n_row_groups;
+    const uint32_t row_tile = (region % (uint32_t)p.n_row_groups) * kGroup + (tau & 7u);
+    if (row_tile < (uint32_t)p.n_row_tiles) {
+      row0 = (int64_t)row_tile * kTileRows;
+      col0 = (int64_t)col_tile * kTileCols;
+      return true;
+    }
+  }
+}
+
+// s_waitcnt immediate for vmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] << 14); the other counters left unconstrained
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// global -> LDS copy of 16 bytes per lane (gfx950 LDS DMA): lane l's bytes
+// land at LDS address m0 + 16 l.  The s_nop covers the M0 write hazard.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// a pointer that is the same in every lane, moved to SGPRs
+__device__ __forceinline__ const uint16_t* wave_uniform(const uint16_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint16_t*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Start copying a tile into an LDS buffer.  Wave w fills rows 8w .. 8w+7, two
+// rows (1 KB) per instruction: lane l writes stored piece l % 32 of row
+// 8w + 2i + l / 32, so it loads the global piece that the swizzle puts there.
+// Pieces outside the tensor are written as zeros instead.
+__device__ __forceinline__ void issue_tile(const QuantParams& p, int64_t row0, int64_t col0, int wave, int lane,
+                                           uint8_t* buf) {
+  const uint16_t* base = wave_uniform(p.x + row0 * p.ld_x + col0);
+  const int ps = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * wave + 2 * i + (lane >> 5);
+    const int pg = ps ^ ((((ps >> 4) & 1) << 1) | (r & 1) | (((r >> 3) & 1) << 2));
+    if (row0 + r < p.rows && col0 + 8 * pg < p.cols)
+      dma16(base, (uint32_t)((r * p.ld_x + 8 * pg) * 2), lds_addr(buf + (8 * wave + 2 * i) * kRowBytes));
+    else
+      *(uint4*)(buf + r * kRowBytes + ps * 16) = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Split two packed bf16 values into (high, low) parts when `two`.
+__device__ __forceinline__ void split_pair(uint32_t w, uint32_t t2, bool two, uint32_t& hi, uint32_t& lo) {
+  lo = two ? split_low(w, t2) : 0u;
+  hi = w ^ lo;
+}
+
+// Scale bytes of 8 consecutive blocks of a row, held by lanes 8a .. 8a+7
+// (k = lane % 8): with 8-byte aligned scale rows and all 8 blocks inside the
+// tensor, the lane with k == 0 writes all 8 at once.  All lanes of the wave
+// must call this (the gather is a cross-lane exchange).
+__device__ __forceinline__ void store_row_scales(uint8_t* dst, int k, uint32_t byte, bool wide, bool active) {
+  uint32_t v = byte << (8 * (k & 3));
+  v |= (uint32_t)__shfl_xor((int)v, 1);
+  v |= (uint32_t)__shfl_xor((int)v, 2);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)v, 4);
+  if (!active) return;
+  if (wide) {
+    if (k == 0) *(uint2*)dst = uint2{v, hi};
+  } else {
+    dst[k] = (uint8_t)byte;
+  }
+}
+
+// Passes in which each lane reads a whole block: no rotation, float64
+// butterflies (kClsF64) or the exact fixed-point path (kClsSpecial).  Row
+// pass: lane (r, k) owns chunk k of row r; column pass: lane c owns column c.
+template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
+__device__ __forceinline__ void lane_block_passes(const QuantParams& p, const uint8_t* hi_part, int t, int64_t row0,
+                                                  int64_t col0, int cls, uint32_t mask, bool wide_scales) {
+  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  const bool full_width = col0 + kTileCols <= p.cols;
+  if (cls != kClsSpecial) {
+    if constexpr (DO_ROW) {
+      const int r = t >> 3, k = t & 7;
+      const int64_t row = row0 + r, c0 = col0 + 32 * k;
+      float y[32];
+      load_rotate<HAD>(
+          [&](int h, float (&x)[16]) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const uint4 v = *(const uint4*)(hi_part + lds_off(r, 32 * k + 16 * h + 8 * q));
+              const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[8 * q + 2 * e] = __uint_as_float(dw[e] << 16);
+                x[8 * q + 2 * e + 1] = __uint_as_float(dw[e] & 0xFFFF0000u);
+              }
+            }
+          },
+          mask, y);
+      uint32_t w[4];
+      const uint32_t byte =
+          cast_block<GRID, ROUND>(y, ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2, 0u, k0, k1, w);
+      const bool valid = row < p.rows && c0 < p.cols;
+      if (valid) *(uint4*)(p.row_codes + row * p.ld_row_codes + c0 / 2) = uint4{w[0], w[1], w[2], w[3]};
+      store_row_scales(p.row_scales + row * p.ld_row_scales + col0 / 32, k, byte, wide_scales && full_width, valid);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DO_COL) {
+      const int64_t col = col0 + t;
+      float y[32];
+      load_rotate<HAD>(
+          [&](int h, float (&x)[16]) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = 16 * h + i;
+              const uint32_t off = j * kRowBytes + lds_col(t, j & 9);
+              x[i] = __uint_as_float((uint32_t)*(const uint16_t*)(hi_part + off) << 16);
+            }
+          },
+          mask, y);
+      uint32_t w[4];
+      const uint32_t byte =
+          cast_block<GRID, ROUND>(y, ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2, 1u, k0, k1, w);
+      if (col < p.cols) {
+        *(uint4*)(p.col_codes + col * p.ld_col_codes + row0 / 2) = uint4{w[0], w[1], w[2], w[3]};
+        p.col_scales[col * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
+      }
+    }
+  } else {
+    if constexpr (DO_ROW) {
+      const int r = t >> 3, k = t & 7;
+      const int64_t row = row0 + r, c0 = col0 + 32 * k;
+      if (row < p.rows && c0 < p.cols)
+        special_block<HAD, GRID, ROUND>(
+            [&](int j) { return (uint32_t)*(const uint16_t*)(hi_part + lds_off(r, 32 * k + j)); }, mask,
+            ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2, 0u, k0, k1,
+            p.row_codes + row * p.ld_row_codes + c0 / 2, p.row_scales + row * p.ld_row_scales + c0 / 32);
+    }
+    if constexpr (DO_COL) {
+      const int64_t col = col0 + t;
+      if (col < p.cols)
+        special_block<HAD, GRID, ROUND>(
+            [&](int j) { return (uint32_t)*(const uint16_t*)(hi_part + lds_off(j, t)); }, mask,
+            ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2, 1u, k0, k1,
+            p.col_codes + col * p.ld_col_codes + row0 / 2, p.col_scales + col * p.ld_col_scales + row0 / 32);
+    }
+  }
+}
+
+template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+quant_kernel(const QuantParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kPartBytes];   // two tile buffers
   __shared__ uint32_t red[2 * (kThreads / 64)];
 
-  // ---- XCD-aware tile order: the 8 row tiles of a 256x256 region run on one
-  // XCD back to back, so the column-wise output's 16-byte pieces of one
-  // 128-byte line are merged in that XCD's L2.
-  const uint32_t wg = blockIdx.x;
-  const uint32_t xcd = wg & 7u, j = wg >> 3;
-  const uint32_t region = (j >> 3) * 8u + xcd, member = j & 7u;
-  const uint32_t n_regions = (uint32_t)p.n_col_tiles * (uint32_t)p.n_row_groups;
-  if (region >= n_regions) return;
-  const uint32_t col_tile = region / (uint32_t)p.n_row_groups;
-  const uint32_t row_tile = (region % (uint32_t)p.n_row_groups) * kGroup + member;
-  if (row_tile >= (uint32_t)p.n_row_tiles) return;
-  const int64_t row0 = (int64_t)row_tile * kTileRows;
-  const int64_t col0 = (int64_t)col_tile * kTileCols;
-  const int t = threadIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t xcd = blockIdx.x & 7u, J = gridDim.x >> 3;
+  uint32_t tau = blockIdx.x >> 3;
+  int64_t row0 = 0, col0 = 0;
+  if (!next_tile(p, xcd, J, tau, row0, col0)) return;
+  issue_tile(p, row0, col0, tid >> 6, tid & 63, lds);
+  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  const bool wide_scales = DO_ROW && ((((uintptr_t)p.row_scales) | (uintptr_t)p.ld_row_scales) & 7u) == 0;
+  const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
+  bf16x8 ha[2];
+  if constexpr (HAD > 0) hadamard_operand<HAD>(p.sign_mask, tid & 63, ha);
+  int cur = 0;
 
-  // ---- 1. load (16 B per lane per row segment), range check, stage fp32 in LDS
-  us2 mx2 = {0, 0}, mn2 = {0xFFFF, 0xFFFF};
-  {
-    const int q = t & 31;                       // 16-byte piece within a 512-byte row segment
-    const int64_t c = col0 + q * 8;
+  for (;;) {
+    // Lane ids and the sign mask pass through an empty asm each tile, so that
+    // the many addresses and sign constants derived from them are computed
+    // where they are used instead of being held in registers across the loop.
+    int t = tid;
+    uint32_t mask = p.sign_mask;
+    asm volatile("" : "+v"(t), "+v"(mask));
+    const int lane = t & 63, wave = t >> 6, hl = lane >> 5, n = lane & 31;
+    uint8_t* buf = lds + cur * kPartBytes;
+
+    // ---- 1. this tile has landed in LDS (every wave's copies), and every wave
+    // is done with the other buffer: start the next tile's copy into it
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    uint32_t tau_next = tau + J;
+    int64_t nrow0 = 0, ncol0 = 0;
+    const bool more = next_tile(p, xcd, J, tau_next, nrow0, ncol0);
+    if (more) issue_tile(p, nrow0, ncol0, wave, lane, lds + (cur ^ 1) * kPartBytes);
+
+    // ---- 2. packed 16-bit max / min-nonzero of |x| over the tile (any 16-byte
+    // pieces will do: lane t reads pieces t, t + 256, ...)
+    us2 mx2 = {0, 0}, mn2 = {0xFFFF, 0xFFFF};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = (t >> 5) + 8 * i;
-      const int64_t row = row0 + r;
-      uint4 d = {0u, 0u, 0u, 0u};
-      if (row < p.rows && c < p.cols) d = *(const uint4*)(p.x + row * p.ld_x + c);
-      const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+      const uint4 v = *(const uint4*)(buf + 16 * (t + kThreads * i));
+      const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        us2 m = __builtin_bit_cast(us2, dw[k] & 0x7FFF7FFFu);
+        const us2 m = __builtin_bit_cast(us2, dw[k] & 0x7FFF7FFFu);
         mx2 = __builtin_elementwise_max(mx2, m);
         mn2 = __builtin_elementwise_min(mn2, m - (us2){1, 1});  // zero wraps to 0xFFFF: ignored
       }
-      float* dst = tile + r * kRowPitch + (q >> 2) * kChunkPitch + (q & 3) * 8;
-      float4 lo = {__uint_as_float(d.x << 16), __uint_as_float(d.x & 0xFFFF0000u),
-                   __uint_as_float(d.y << 16), __uint_as_float(d.y & 0xFFFF0000u)};
-      float4 hi = {__uint_as_float(d.z << 16), __uint_as_float(d.z & 0xFFFF0000u),
-                   __uint_as_float(d.w << 16), __uint_as_float(d.w & 0xFFFF0000u)};
-      *(float4*)dst = lo;
-      *(float4*)(dst + 4) = hi;
     }
-  }
-  uint32_t mx = max((uint32_t)mx2.x, (uint32_t)mx2.y);
-  uint32_t mn = min((uint32_t)mn2.x, (uint32_t)mn2.y);
+    uint32_t mx = max((uint32_t)mx2.x, (uint32_t)mx2.y);
+    uint32_t mn = min((uint32_t)mn2.x, (uint32_t)mn2.y);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-  }
-  if ((t & 63) == 0) {
-    red[t >> 6] = mx;
-    red[4 + (t >> 6)] = mn;
-  }
-  __syncthreads();
-  mx = max(max(red[0], red[1]), max(red[2], red[3]));
-  mn = min(min(red[4], red[5]), min(red[6], red[7]));
-  // special tile: non-finite or near-overflow inputs, or (rotating) a span the
-  // float64 butterfly cannot hold exactly
-  bool careful = mx >= (250u << 7);
-  if constexpr (HAD > 0) {
-    if (mn != 0xFFFFu) {
+    for (int o = 32; o >= 1; o >>= 1) {
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    }
+    if (lane == 0) {
+      red[wave] = mx;
+      red[4 + wave] = mn;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    mn = min(min(red[4], red[5]), min(red[6], red[7]));
+
+    // ---- 3. classify by the exponent fields of the largest and smallest nonzero |x|
+    int cls = kClsMfma1;
+    uint32_t t2 = 0;                                // split threshold (both halves)
+    if (mx >= (250u << 7)) {
+      cls = kClsSpecial;                            // Inf/NaN or sums that could overflow
+    } else if (HAD > 0 && mn != 0xFFFFu) {
       const int fmax = max((int)(mx >> 7), 1);
       const int fmin = max((int)((mn + 1u) >> 7), 1);
-      careful |= (fmax - fmin) > 40;
-    }
-  }
-
-  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
-
-  // ---- 2. row pass: lane (r, k) owns chunk k of row r
-  if constexpr (DO_ROW) {
-    const int r = t >> 3, k = t & 7;
-    const int64_t row = row0 + r, c0 = col0 + k * 32;
-    if (row < p.rows && c0 < p.cols) {
-      float y[32];
-      const float* src = tile + r * kRowPitch + k * kChunkPitch;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = *(const float4*)(src + 4 * i);
-        y[4 * i] = v.x; y[4 * i + 1] = v.y; y[4 * i + 2] = v.z; y[4 * i + 3] = v.w;
+      const int span = fmax - fmin;
+      if (span > 40) cls = kClsSpecial;
+      else if (fmin < 8 || span > 23) cls = kClsF64;
+      else if (span > 11) {
+        cls = kClsMfma2;
+        t2 = (uint32_t)(fmax - 11) << 7;
+        t2 |= t2 << 16;
       }
+    }
+
+    const bool full_width = col0 + kTileCols <= p.cols;
+    if (HAD > 0 && (cls == kClsMfma1 || cls == kClsMfma2)) {
       if constexpr (HAD > 0) {
-        if (!careful) rotate_fast<HAD, RHT>(y, p.sign_mask);
-        else rotate_exact<HAD>(y, RHT ? p.sign_mask : 0u);
-      }
-      uint32_t u[32];
-      if constexpr (ROUND == MX_ROUND_SR) philox_words32((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0, 0u, k0, k1, u);
-      uint32_t w[4];
-      const uint32_t byte = cast_block<GRID, ROUND>(y, careful, u, w);
-      *(uint4*)(p.row_codes + row * p.ld_row_codes + c0 / 2) = uint4{w[0], w[1], w[2], w[3]};
-      p.row_scales[row * p.ld_row_scales + c0 / 32] = (uint8_t)byte;
-    }
-  }
-
-  // ---- 3. column pass: lane c owns column c of the tile (32 rows = one block)
-  if constexpr (DO_COL) {
-    const int64_t col = col0 + t;
-    if (col < p.cols) {
-      float y[32];
-      const float* src = tile + (t >> 5) * kChunkPitch + (t & 31);
+        const bool two = cls == kClsMfma2;
+        // ---- 4a. row pass on the matrix cores: wave w, group g = blocks of
+        // rows 8w + 4g .. +3 (8 blocks per row)
+        if constexpr (DO_ROW) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] = src[i * kRowPitch];
-      if constexpr (HAD > 0) {
-        if (!careful) rotate_fast<HAD, RHT>(y, p.sign_mask);
-        else rotate_exact<HAD>(y, RHT ? p.sign_mask : 0u);
+          for (int g = 0; g < 2; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int r = 8 * wave + 4 * g + (n >> 3), k = n & 7;
+            uint4 bh[2], bl[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint4 v = *(const uint4*)(buf + r * kRowBytes +
+                                              lds_col(32 * k + 16 * h + 8 * hl, ((n >> 3) & 1) | ((wave & 1) << 3)));
+              split_pair(v.x, t2, two, bh[h].x, bl[h].x);
+              split_pair(v.y, t2, two, bh[h].y, bl[h].y);
+              split_pair(v.z, t2, two, bh[h].z, bl[h].z);
+              split_pair(v.w, t2, two, bh[h].w, bl[h].w);
+            }
+            float y[16];
+            if (two) mfma_block_sums<true>(ha, bh, bl, c, y);
+            else mfma_block_sums<false>(ha, bh, bl, c, y);
+            const int64_t row = row0 + r, c0 = col0 + 32 * k;
+            const bool valid = row < p.rows && c0 < p.cols;
+            uint32_t w[2];
+            const uint32_t byte = cast_half_block<GRID, ROUND>(
+                y, lane, (((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2) + 4 * hl, 0u, k0, k1, w);
+            if (valid) *(uint2*)(p.row_codes + row * p.ld_row_codes + c0 / 2 + 8 * hl) = uint2{w[0], w[1]};
+            store_row_scales(p.row_scales + row * p.ld_row_scales + col0 / 32, k, byte, wide_scales && full_width,
+                             valid && hl == 0);
+          }
+        }
+        // ---- 4b. column pass on the matrix cores: wave w, group g = columns
+        // 64w + 32g .. +31
+        if constexpr (DO_COL) {
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int cc = 64 * wave + 32 * g + n;
+            const uint32_t cb0 = lds_col(cc, hl << 3), cb1 = lds_col(cc, (hl << 3) | 1);
+            uint4 bh[2], bl[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              uint32_t vh[4], vl[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int j = 16 * h + 8 * hl + 2 * e;
+                const uint32_t v = (uint32_t)*(const uint16_t*)(buf + j * kRowBytes + cb0) |
+                                   ((uint32_t)*(const uint16_t*)(buf + (j + 1) * kRowBytes + cb1) << 16);
+                split_pair(v, t2, two, vh[e], vl[e]);
+              }
+              bh[h] = uint4{vh[0], vh[1], vh[2], vh[3]};
+              bl[h] = uint4{vl[0], vl[1], vl[2], vl[3]};
+            }
+            float y[16];
+            if (two) mfma_block_sums<true>(ha, bh, bl, c, y);
+            else mfma_block_sums<false>(ha, bh, bl, c, y);
+            const int64_t col = col0 + cc;
+            uint32_t w[2];
+            const uint32_t byte = cast_half_block<GRID, ROUND>(
+                y, lane, (((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2) + 4 * hl, 1u, k0, k1, w);
+            if (col < p.cols) {
+              *(uint2*)(p.col_codes + col * p.ld_col_codes + row0 / 2 + 8 * hl) = uint2{w[0], w[1]};
+              if (hl == 0) p.col_scales[col * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
+            }
+          }
+        }
       }
-      uint32_t u[32];
-      if constexpr (ROUND == MX_ROUND_SR) philox_words32((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0, 1u, k0, k1, u);
-      uint32_t w[4];
-      const uint32_t byte = cast_block<GRID, ROUND>(y, careful, u, w);
-      *(uint4*)(p.col_codes + col * p.ld_col_codes + row0 / 2) = uint4{w[0], w[1], w[2], w[3]};
-      p.col_scales[col * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
+    } else {
+      // ---- 4c. no rotation, float64 butterflies or exact fixed point: each
+      // lane casts whole blocks
+      lane_block_passes<HAD, GRID, ROUND, DO_ROW, DO_COL>(p, buf, t, row0, col0, cls, mask, wide_scales);
     }
+    if (!more) break;
+    tau = tau_next;
+    row0 = nrow0;
+    col0 = ncol0;
+    cur ^= 1;
   }
 }
 
 // ---- host-side launch: pick the instantiation
-template <int HAD, bool RHT, int GRID, int ROUND>
+template <int HAD, int GRID, int ROUND>
 static hipError_t launch_axes(const QuantParams& p, bool do_row, bool do_col, dim3 grid, hipStream_t s) {
   if (do_row && do_col)
-    hipLaunchKernelGGL((quant_tile_kernel<HAD, RHT, GRID, ROUND, true, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((quant_kernel<HAD, GRID, ROUND, true, true>), grid, dim3(kThreads), 0, s, p);
   else if (do_row)
-    hipLaunchKernelGGL((quant_tile_kernel<HAD, RHT, GRID, ROUND, true, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((quant_kernel<HAD, GRID, ROUND, true, false>), grid, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((quant_tile_kernel<HAD, RHT, GRID, ROUND, false, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((quant_kernel<HAD, GRID, ROUND, false, true>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
-template <int HAD, bool RHT>
+template <int HAD>
 static hipError_t launch_cast(const QuantParams& p, int grid_kind, int round, bool r, bool c, dim3 g, hipStream_t s) {
   if (grid_kind == MX_GRID_E2M1) {
-    return round == MX_ROUND_RTNE ? launch_axes<HAD, RHT, MX_GRID_E2M1, MX_ROUND_RTNE>(p, r, c, g, s)
-                                  : launch_axes<HAD, RHT, MX_GRID_E2M1, MX_ROUND_SR>(p, r, c, g, s);
+    return round == MX_ROUND_RTNE ? launch_axes<HAD, MX_GRID_E2M1, MX_ROUND_RTNE>(p, r, c, g, s)
+                                  : launch_axes<HAD, MX_GRID_E2M1, MX_ROUND_SR>(p, r, c, g, s);
   }
-  return round == MX_ROUND_RTNE ? launch_axes<HAD, RHT, MX_GRID_E1M2, MX_ROUND_RTNE>(p, r, c, g, s)
-                                : launch_axes<HAD, RHT, MX_GRID_E1M2, MX_ROUND_SR>(p, r, c, g, s);
+  return round == MX_ROUND_RTNE ? launch_axes<HAD, MX_GRID_E1M2, MX_ROUND_RTNE>(p, r, c, g, s)
+                                : launch_axes<HAD, MX_GRID_E1M2, MX_ROUND_SR>(p, r, c, g, s);
 }
 
 hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int round, bool do_row, bool do_col,
@@ -347,14 +754,18 @@ hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int r
   p.n_col_tiles = (int32_t)((p.cols + kTileCols - 1) / kTileCols);
   p.n_row_groups = (p.n_row_tiles + kGroup - 1) / kGroup;
   const int64_t regions = (int64_t)p.n_col_tiles * p.n_row_groups;
-  // WG ids: 8 consecutive regions x 8 members per 64 ids
-  const int64_t wgs = ((regions + 7) / 8) * 64;
-  const dim3 g((unsigned)wgs);
-  if (had_n == 0) return launch_cast<0, false>(p, grid_kind, round, do_row, do_col, g, s);
-  if (had_n == 16) return rht ? launch_cast<16, true>(p, grid_kind, round, do_row, do_col, g, s)
-                              : launch_cast<16, false>(p, grid_kind, round, do_row, do_col, g, s);
-  return rht ? launch_cast<32, true>(p, grid_kind, round, do_row, do_col, g, s)
-             : launch_cast<32, false>(p, grid_kind, round, do_row, do_col, g, s);
+  // tiles each XCD walks: its regions (every 8th) x 8 row tiles
+  const int64_t per_xcd = ((regions + 7) / 8) * kGroup;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t wgs_per_xcd = std::max<int64_t>(1, (int64_t)cus * kWgPerCu / 8);
+  const dim3 g((unsigned)(8 * std::min(per_xcd, wgs_per_xcd)));
+  if (!rht) p.sign_mask = 0u;
+  if (had_n == 0) return launch_cast<0>(p, grid_kind, round, do_row, do_col, g, s);
+  if (had_n == 16) return launch_cast<16>(p, grid_kind, round, do_row, do_col, g, s);
+  return launch_cast<32>(p, grid_kind, round, do_row, do_col, g, s);
 }
 
 }  // namespace mx

@@ -90,7 +90,7 @@ typedef struct {
  *   rows, cols >= 0 (either 0: nothing to do, MX_OK); cols % 8 == 0;
  *              cols % block == 0 if the row-wise output is requested,
  *              rows % block == 0 if the column-wise output is requested
- *   ld_x       elements between rows; >= cols, multiple of 8
+ *   ld_x       elements between rows; >= cols, multiple of 8, below 2^25
  *   block      32 (the MX block; 16 returns MX_ERR_UNSUPPORTED)
  *   grid       MX_GRID_E2M1 or MX_GRID_E1M2
  *   round      MX_ROUND_RTNE or MX_ROUND_SR (seed keys the Philox draws)

@@ -54,6 +54,7 @@ def quant(x=FAKE, rows=32, cols=128, ld=128, block=32, grid=0, rnd=0, axis=1, rq
     (dict(rows=-1), 1), (dict(cols=-5), 1), (dict(grid=7), 1), (dict(rnd=9), 1), (dict(axis=0), 1),
     (dict(axis=4), 1), (dict(block=64), 1), (dict(x=0), 1), (dict(x=FAKE + 2), 1),
     (dict(ld=100), 1), (dict(cols=120, ld=128), 1),          # row output needs cols % 32
+    (dict(ld=1 << 25), 1),                                      # row pitch below 2^25 elements
     (dict(cols=12, ld=16, axis=2), 1),                          # cols % 8
     (dict(rows=40, axis=2), 1),                                 # column output needs rows % 32
     (dict(rq=None), 1), (dict(rq=q(codes=FAKE + 8)), 1), (dict(rq=q(ld_codes=32)), 1),
