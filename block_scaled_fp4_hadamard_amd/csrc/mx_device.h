@@ -18,14 +18,19 @@ constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
 struct U4 { uint32_t x, y, z, w; };
 
+// a ^ b ^ c in one gfx950 three-input bit operation (truth table 0x96)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                             uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)c0 * kPhiloxM0;
     const uint64_t p1 = (uint64_t)c2 * kPhiloxM1;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -34,6 +39,41 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
     k1 += kPhiloxW1;
   }
   return U4{c0, c1, c2, c3};
+}
+
+// Philox4x32-10 of the four counters (ctr + q, stream, 0), q = 0..3 (ctr is
+// the 64-bit block index in the first two counter words), run in lockstep:
+// the four dependency chains of multiplies interleave instead of waiting on
+// one another.
+__device__ __forceinline__ void philox4x32_10_x4(uint64_t ctr, uint32_t stream, uint32_t k0, uint32_t k1,
+                                                 U4 (&out)[4]) {
+  uint32_t c0[4], c1[4], c2[4], c3[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t b = ctr + (uint64_t)q;
+    c0[q] = (uint32_t)b;
+    c1[q] = (uint32_t)(b >> 32);
+    c2[q] = stream;
+    c3[q] = 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t p0 = (uint64_t)c0[q] * kPhiloxM0;
+      const uint64_t p1 = (uint64_t)c2[q] * kPhiloxM1;
+      const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1[q], k0);
+      const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3[q], k1);
+      c1[q] = (uint32_t)p1;
+      c3[q] = (uint32_t)p0;
+      c0[q] = n0;
+      c2[q] = n2;
+    }
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = U4{c0[q], c1[q], c2[q], c3[q]};
 }
 
 // ---------------------------------------------------------------------------

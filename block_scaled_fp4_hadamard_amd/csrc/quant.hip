@@ -156,19 +156,23 @@ __device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ct
     }
   } else {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    for (int hh = 0; hh < 2; ++hh) {                 // 16 outputs (four Philox blocks) at a time
+      uint32_t u[16] = {};
       if constexpr (ROUND == MX_ROUND_SR) {
-        const uint64_t b0 = ctr + 2 * d, b1 = b0 + 1;
-        const U4 r0 = philox4x32_10((uint32_t)b0, (uint32_t)(b0 >> 32), stream, 0u, k0, k1);
-        const U4 r1 = philox4x32_10((uint32_t)b1, (uint32_t)(b1 >> 32), stream, 0u, k0, k1);
-        u[0] = r0.x; u[1] = r0.y; u[2] = r0.z; u[3] = r0.w;
-        u[4] = r1.x; u[5] = r1.y; u[6] = r1.z; u[7] = r1.w;
-      }
-      uint32_t r = 0;
+        U4 r[4];
+        philox4x32_10_x4(ctr + 4 * hh, stream, k0, k1, r);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) r |= cast_one<GRID, ROUND>(y[8 * d + q], byte, u[q]) << (4 * q);
-      w[d] = r;
+        for (int q = 0; q < 4; ++q) {
+          u[4 * q + 0] = r[q].x; u[4 * q + 1] = r[q].y; u[4 * q + 2] = r[q].z; u[4 * q + 3] = r[q].w;
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r |= cast_one<GRID, ROUND>(y[16 * hh + 8 * d + q], byte, u[8 * d + q]) << (4 * q);
+        w[2 * hh + d] = r;
+      }
     }
   }
   return byte;
@@ -312,19 +316,20 @@ __device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int la
       w[d] = r;
     }
   } else {
+    uint32_t u[16] = {};
+    if constexpr (ROUND == MX_ROUND_SR) {
+      U4 r[4];
+      philox4x32_10_x4(ctr, stream, k0, k1, r);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u[4 * q + 0] = r[q].x; u[4 * q + 1] = r[q].y; u[4 * q + 2] = r[q].z; u[4 * q + 3] = r[q].w;
+      }
+    }
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      uint32_t u[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-      if constexpr (ROUND == MX_ROUND_SR) {
-        const uint64_t b0 = ctr + 2 * d, b1 = b0 + 1;
-        const U4 r0 = philox4x32_10((uint32_t)b0, (uint32_t)(b0 >> 32), stream, 0u, k0, k1);
-        const U4 r1 = philox4x32_10((uint32_t)b1, (uint32_t)(b1 >> 32), stream, 0u, k0, k1);
-        u[0] = r0.x; u[1] = r0.y; u[2] = r0.z; u[3] = r0.w;
-        u[4] = r1.x; u[5] = r1.y; u[6] = r1.z; u[7] = r1.w;
-      }
       uint32_t r = 0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) r |= cast_one<GRID, ROUND>(y[8 * d + q], byte, u[q]) << (4 * q);
+      for (int q = 0; q < 8; ++q) r |= cast_one<GRID, ROUND>(y[8 * d + q], byte, u[8 * d + q]) << (4 * q);
       w[d] = r;
     }
   }

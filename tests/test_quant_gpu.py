@@ -94,6 +94,34 @@ def test_edge_cases(had_n, had_kind, rounding):
               had_seed=99)
 
 
+def span_tiles(signs):
+    """256 x 256 bf16: eight 32-row tiles whose inputs span exactly 11, 12, 23, 24, 40 and 41 binades, one
+    with values down to 2^-121 and one just under 2^123.  Every row block and column block of a tile holds
+    both extremes; significands are all ones (or random) so that the sums need every bit of an fp32
+    significand at the top of the exact range."""
+    rng = np.random.default_rng(23)
+    spans = [11, 12, 23, 24, 40, 41, 8, 5]
+    emaxs = [3, 0, 10, -4, 20, 20, -113, 122]
+    bits = np.zeros((256, 256), dtype=np.uint16)
+    r = np.arange(32)[:, None]
+    c = np.arange(256)[None, :]
+    for t, (span, emax) in enumerate(zip(spans, emaxs)):
+        e = emax - ((r + c) % (span + 1))
+        man = np.full((32, 256), 0x7F) if t % 2 == 0 else rng.integers(0, 128, (32, 256)) | 1
+        sgn = (rng.random((32, 256)) < 0.5) if signs else np.zeros((32, 256), dtype=bool)
+        bits[32 * t:32 * t + 32] = (sgn.astype(np.uint16) << 15) | ((e + 127).astype(np.uint16) << 7) | man
+    return bits
+
+
+@pytest.mark.parametrize("had_n,had_kind", [(16, "det"), (32, "det"), (32, "rand")])
+@pytest.mark.parametrize("signs", [False, True])
+def test_exact_sum_boundaries(had_n, had_kind, signs):
+    """Tiles at each edge of the matrix-core (one part, two parts), float64 and fixed-point paths."""
+    bits = span_tiles(signs)
+    check(bits, "spans", axis="both", had_n=had_n, had_kind=had_kind, had_seed=4)
+    check(bits, "spans-sr", axis="both", had_n=had_n, had_kind=had_kind, had_seed=4, rounding="sr", seed=8)
+
+
 def test_repeatable():
     bits = synth.activation(64, 512, np.random.default_rng(1))
     x = to_gpu_bits(bits)
