@@ -11,6 +11,7 @@ Inputs are seeded synthetic tensors of the real shapes, resident in HBM
 before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --calibrate-copy BYTES     (device copies of BYTES, for traffic-counter scaling)
 
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
@@ -41,11 +42,39 @@ def parse():
     ap.add_argument("--grid", default="e2m1", choices=["e2m1", "e1m2"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=8192)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     return ap.parse_args()
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def calibrate_copy(nbytes):
+    """Three plain device-to-device copies of nbytes (after one warm-up), nothing else."""
+    import torch
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log("copied %d bytes 3 times" % nbytes)
+    return 0
+
+
+def load_traffic(family):
+    """HBM bytes per launch of a kernel family from profiles/traffic.json, or None when the file is
+    missing or was measured on different kernel sources."""
+    try:
+        from block_scaled_fp4_hadamard_amd.rocprof_summary import sources_hash
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("sources_hash") != sources_hash():
+            return None
+        return t["families"][family]["bytes_per_launch"]
+    except Exception:
+        return None
 
 
 def cpu_baseline(tokens=512):
@@ -80,6 +109,8 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
     import numpy as np
     import torch
     from block_scaled_fp4_hadamard_amd import synth
@@ -141,12 +172,7 @@ def main():
     dom = max(fam, key=lambda lb: fam[lb]["ms"])
     f = fam[dom]
     avg_s = f["ms"] / f["launches"] * 1e-3
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            traffic = json.load(open(TRAFFIC_FILE)).get(dom)
-        except Exception:
-            traffic = None
+    traffic = load_traffic(dom)
     if f["flops"]:
         achieved = f["flops"] / f["launches"] / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
