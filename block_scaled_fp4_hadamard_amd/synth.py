@@ -98,21 +98,27 @@ def mlp(tokens=TOKENS, ffn=D_FFN, d=D_MODEL):
             "x": activation(tokens, ffn, _rng("mlp", 2))}
 
 
-def llama_block(tokens=TOKENS):
+def llama_block(tokens=TOKENS, only=None):
     """Every operand of one Llama-3.1-8B block's seven linears, keyed by name.
 
     Inputs shared by several linears in the model are drawn once
-    (x_attn for q/k/v, x_mlp for gate/up).
+    (x_attn for q/k/v, x_mlp for gate/up).  only: draw just the operands of
+    these linears (the same values as in the whole block).
     """
     out = {}
     ordinal = 0
     in_dims = {"x_attn": D_MODEL, "x_o": D_MODEL, "x_mlp": D_MODEL, "x_down": D_FFN}
+    needed = None if only is None else {LLAMA_INPUT_OF[lin] for lin in only}
     for name, cols in in_dims.items():
-        out[name] = activation(tokens, cols, _rng("llama_block", ordinal))
+        if needed is None or name in needed:
+            out[name] = activation(tokens, cols, _rng("llama_block", ordinal))
         ordinal += 1
     for lin, (o, i) in LLAMA_LINEARS.items():
-        out["w_" + lin] = weight(o, i, _rng("llama_block", ordinal))
+        take = only is None or lin in only
+        if take:
+            out["w_" + lin] = weight(o, i, _rng("llama_block", ordinal))
         ordinal += 1
-        out["dy_" + lin] = gradient(tokens, o, _rng("llama_block", ordinal))
+        if take:
+            out["dy_" + lin] = gradient(tokens, o, _rng("llama_block", ordinal))
         ordinal += 1
     return out

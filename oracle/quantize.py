@@ -88,10 +88,12 @@ def block_scale_exponents(amax, grid):
 
 
 def quantize_lines(bits, grid=E2M1, rounding=RTNE, seed=0, stream=STREAM_ROW_SR,
-                   had_n=0, signs=None, block=32):
+                   had_n=0, signs=None, block=32, line_ids=None):
     """Quantize every line (row) of a 2-D bf16 array along its last axis.
 
-    bits: (lines, length) uint16 bf16 patterns.
+    bits: (lines, length) uint16 bf16 patterns.  line_ids: the index of each
+    given line in the whole output (default 0, 1, ...), which only enters the
+    stochastic-rounding element index.
     Returns (codes, scales): codes (lines, ceil(length/2)) uint8 with element
     2j in the low nibble of byte j; scales (lines, ceil(length/block)) uint8.
     """
@@ -126,7 +128,8 @@ def quantize_lines(bits, grid=E2M1, rounding=RTNE, seed=0, stream=STREAM_ROW_SR,
     if rounding == RTNE:
         mag = rtne_magnitude_codes(v, grid)
     else:
-        idx = (np.arange(lines, dtype=np.uint64)[:, None] * np.uint64(length)
+        ids = np.arange(lines) if line_ids is None else np.asarray(line_ids)
+        idx = (ids.astype(np.uint64)[:, None] * np.uint64(length)
                + np.arange(nblk * block, dtype=np.uint64)[None, :])
         u = uniform_words(seed, stream, idx).reshape(lines, nblk, block)
         mag = sr_magnitude_codes(v, u, grid)
@@ -143,23 +146,29 @@ def quantize_lines(bits, grid=E2M1, rounding=RTNE, seed=0, stream=STREAM_ROW_SR,
 
 
 def quantize_ref(x_bits, axis="row", grid=E2M1, rounding=RTNE, seed=0,
-                 had_n=0, had_kind="det", had_seed=0, block=32):
+                 had_n=0, had_kind="det", had_seed=0, block=32, lines=None):
     """Quantize a (rows, cols) bf16 tensor row-wise, column-wise or both.
 
     Returns {"row": (codes, scales), "col": (codes, scales)} with the requested
     keys.  Row-wise blocks run along columns (codes (rows, cols/2)); column-wise
     blocks run along rows and are stored transposed (codes (cols, rows/2)).
     With had_kind "rand" every rotation uses the same sign vector from had_seed.
+    lines (one axis only): quantize just these output lines (rows for "row",
+    columns for "col"), in that order; the result equals those lines of the
+    whole output.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     assert axis in ("row", "col", "both")
+    assert lines is None or axis != "both"
     signs = rht_signs(had_n, had_seed) if (had_n and had_kind == "rand") else None
     out = {}
     if axis in ("row", "both"):
-        out["row"] = quantize_lines(x_bits, grid, rounding, seed, STREAM_ROW_SR, had_n, signs, block)
+        src = x_bits if lines is None else x_bits[np.asarray(lines)]
+        out["row"] = quantize_lines(src, grid, rounding, seed, STREAM_ROW_SR, had_n, signs, block, lines)
     if axis in ("col", "both"):
-        out["col"] = quantize_lines(np.ascontiguousarray(x_bits.T), grid, rounding, seed,
-                                    STREAM_COL_SR, had_n, signs, block)
+        src = x_bits.T if lines is None else x_bits[:, np.asarray(lines)].T
+        out["col"] = quantize_lines(np.ascontiguousarray(src), grid, rounding, seed,
+                                    STREAM_COL_SR, had_n, signs, block, lines)
     return out
 
 

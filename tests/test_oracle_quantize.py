@@ -8,6 +8,7 @@ from oracle import formats as F
 from oracle.quantize import quantize_ref, quantize_lines, RTNE, SR, cast_scalar
 from oracle.gemm import decode
 from block_scaled_fp4_hadamard_amd.synth import f32_to_bf16_bits
+from block_scaled_fp4_hadamard_amd import synth
 
 
 def _unpack(codes, length):
@@ -141,3 +142,16 @@ def test_rtne_codes_decode_to_nearest_level():
         dmin = np.abs(cand - xv[:, :, None]).min(axis=2)
         clamp = np.abs(xv) > lv[-1] * scale
         assert np.all((np.abs(dec - xv) <= dmin + 0) | clamp)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_selected_lines_equal_lines_of_whole_output(axis):
+    """Quantizing a subset of output lines (as the full-size GPU tests do) gives exactly those lines of the
+    whole output, stochastic rounding included (the element index keeps the line's place)."""
+    rng = np.random.default_rng(4)
+    x = synth.activation(64, 96, rng)
+    whole = quantize_ref(x, axis, rounding="sr", seed=11, had_n=32)[axis]
+    n_lines = x.shape[0] if axis == "row" else x.shape[1]
+    pick = rng.choice(n_lines, 9, replace=False)
+    part = quantize_ref(x, axis, rounding="sr", seed=11, had_n=32, lines=pick)[axis]
+    assert np.array_equal(part[0], whole[0][pick]) and np.array_equal(part[1], whole[1][pick])
