@@ -24,14 +24,18 @@
 // sum fits fp32's 24-bit significand, so the fp32 accumulation is exact.
 // Tiles spanning 12..23 binades are split by magnitude into a high part
 // (within 11 binades of the tile maximum) and a low part, each product exact,
-// and RN32(S_hi + S_lo) = RN32(S) takes one fp32 add.  Wider tiles (and tiles
-// with values below 2^-119, whose partial sums could be subnormal) take
-// float64 butterflies, exact up to a 40-binade span; non-finite,
-// near-overflow and wider tiles take an exact fixed-point path.
+// and RN32(S_hi + S_lo) = RN32(S) takes one fp32 add.  Tiles spanning 24..35
+// binades take a third part; the three exact fp32 sums then add exactly in
+// float64 (at most 48 significant bits) before the one rounding to fp32.
+// Wider tiles (and tiles with values below 2^-119, whose partial sums could be
+// subnormal) take float64 butterflies, exact up to a 40-binade span;
+// non-finite, near-overflow and wider tiles take an exact fixed-point path.
 //
-// The E2M1 round-to-nearest-even cast uses gfx950's scaled fp4 conversion
-// (ties to even, saturating, dividing by the power-of-two scale given as a
-// float); stochastic rounding and the uniform grid run in plain VALU code.
+// The E2M1 casts use gfx950's scaled fp4 conversions, which divide by the
+// power-of-two scale given as a float and saturate: ties to even for RTNE,
+// and for stochastic rounding the add-and-truncate rule above with the top
+// 22 bits of each element's own Philox word.  The uniform grid runs in plain
+// VALU code.
 //
 // Tile order is XCD-aware: workgroup w runs on XCD w % 8, and the 8 row tiles
 // of a 256x256 region are all taken by workgroups of one XCD at about the
@@ -57,17 +61,22 @@ constexpr int kThreads = 256;
 constexpr int kRowBytes = 2 * kTileCols;           // one tile row of bf16 in LDS
 constexpr int kPartBytes = kTileRows * kRowBytes;  // one staged copy of the tile (16 KB)
 constexpr int kGroup = 8;                          // row tiles of one region (256 rows)
-constexpr int kWgPerCu = 4;                        // resident workgroups per CU in the persistent grid
 
 // fp32 RN32(1/sqrt(32)) = sqrt(2)/8 and 1/sqrt(16)
 constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;
 constexpr float kInvSqrt16 = 0.25f;
 
+// Resident workgroups per CU in the persistent grid (one wave of each per
+// SIMD): four, or three for stochastic rounding, whose Philox draws need the
+// larger register budget.
+constexpr int wgs_per_cu(int round) { return round == MX_ROUND_SR ? 3 : 4; }
+
 // tile classes (uniform per tile)
 constexpr int kClsMfma1 = 0;     // matrix-core sums, one part (or no rotation)
 constexpr int kClsMfma2 = 1;     // matrix-core sums, high + low parts
-constexpr int kClsF64 = 2;       // float64 butterflies
-constexpr int kClsSpecial = 3;   // exact fixed point, careful casting
+constexpr int kClsMfma3 = 2;     // matrix-core sums, high + middle + low parts
+constexpr int kClsF64 = 3;       // float64 butterflies
+constexpr int kClsSpecial = 4;   // exact fixed point, careful casting
 
 __device__ __forceinline__ uint32_t e8m0_scale_bits(uint32_t byte) {
   // the float whose exponent the scaled conversions divide by: 2^(byte-127)
@@ -89,40 +98,33 @@ __device__ __forceinline__ uint32_t lds_off(int r, int c) { return (uint32_t)(r 
 
 // 4-bit code of one value y of a block with scale byte `byte` (finite y):
 // sign bit 3, magnitude code = |y| / 2^(byte-127) on the grid, rounded by
-// RTNE or (SR) up iff the random word u is below floor(frac * 2^32).
+// RTNE, or (SR) up from the level below iff floor(frac * 2^22) + (u >> 10)
+// >= 2^22 for the element's random word u; saturating at the top level.
 template <int GRID, int ROUND>
 __device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u) {
-  const int ebias = (int)byte - 127;
-  uint32_t k;
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const float sc = __uint_as_float(e8m0_scale_bits(byte));
   if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
-    k = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yy, 0.0f, __uint_as_float(e8m0_scale_bits(byte)), 0) & 0xFu;
-    return k;
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yy, 0.0f, sc, 0) & 0xFu;
   } else if constexpr (GRID == MX_GRID_E2M1) {
-    // Stochastic rounding in plain arithmetic.  v = |y| / 2^e (exact unless
-    // v < 2^-126, where P below is 0 either way); the quantum q is 1/2 on
-    // [0,2), 1 on [2,4), 2 on [4,8); t = v / q, lo = floor(t) and
-    // P = floor((t - lo) * 2^32) (t - lo is exact); round up iff u < P.  The
-    // magnitude code of lo is floor(t) + 2*log2(q) + 2 on every piece.
-    // (gfx950's stochastic fp4 conversion is not used: it draws only 22 of
-    // the 32 random bits, a coarser rule than this one.)
-    const float v = ldexpf(fabsf(yy), -ebias);
-    const int qexp = max((int)(__float_as_uint(v) >> 23) - 128, -1);
-    const float t = ldexpf(v, -qexp);
-    const float fl = floorf(t);
-    const uint32_t pr = (uint32_t)ldexpf(t - fl, 32);
-    k = (uint32_t)fl + (uint32_t)(2 * qexp + 2) + (u < pr ? 1u : 0u);
+    // gfx950's stochastic fp4 conversion applies exactly this rule (the
+    // element's own word; the pair's second value is a placeholder, and the
+    // other result bytes are not kept)
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (v2f){yy, 0.0f}, u, sc, 0) & 0xFu;
   } else {
     // uniform grid: magnitude code = |y| * 2^(2-e), rounded
+    const int ebias = (int)byte - 127;
     const float t = ldexpf(fabsf(yy), 2 - ebias);
+    uint32_t k;
     if constexpr (ROUND == MX_ROUND_RTNE) {
       k = (uint32_t)rintf(t);
     } else {
       const float fl = floorf(t);
-      const uint32_t pr = (uint32_t)ldexpf(t - fl, 32);       // floor(frac * 2^32)
-      k = (uint32_t)fl + (u < pr ? 1u : 0u);
+      const uint32_t p22 = (uint32_t)ldexpf(t - fl, 22);     // floor(frac * 2^22); t - fl is exact
+      k = (uint32_t)fl + ((p22 + (u >> 10)) >> 22);
     }
+    return min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
   }
-  return min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
 }
 
 // Scale byte of a block whose largest |y| has float exponent field expf.
@@ -336,22 +338,56 @@ __device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int la
   return byte;
 }
 
-// Row sums of 32 blocks on the matrix cores: b[h] holds the lane's inputs
-// 16h + 8(l / 32) .. +7 of block l % 32 (high part, and low part when TWO).
-template <bool TWO>
-__device__ __forceinline__ void mfma_block_sums(const bf16x8 (&ha)[2], const uint4 (&bh)[2], const uint4 (&bl)[2],
-                                                float c, float (&y)[16]) {
-  f32x16 hi = {}, lo = {};
+// Row sums of 32 blocks on the matrix cores: part[p][h] holds the lane's
+// inputs 16h + 8(l / 32) .. +7 of block l % 32, split into PARTS magnitude
+// parts (high first).  Each part's sum is exact in fp32; two exact parts add
+// with one fp32 rounding, three add exactly in float64 first.
+template <int PARTS>
+__device__ __forceinline__ void mfma_block_sums(const bf16x8 (&ha)[2], const uint4 (&part)[3][2], float c,
+                                                float (&y)[16]) {
+  f32x16 acc[PARTS];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[h], __builtin_bit_cast(bf16x8, bh[h]), hi, 0, 0, 0);
-    if constexpr (TWO) lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[h], __builtin_bit_cast(bf16x8, bl[h]), lo, 0, 0, 0);
-  }
+  for (int q = 0; q < PARTS; ++q) acc[q] = f32x16{};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q)
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[h], __builtin_bit_cast(bf16x8, part[q][h]), acc[q], 0, 0, 0);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float s = TWO ? hi[r] + lo[r] : hi[r];    // both exact: one rounding, RN32(S)
+    float s;
+    if constexpr (PARTS == 1) s = acc[0][r];
+    else if constexpr (PARTS == 2) s = acc[0][r] + acc[1][r];                 // RN32(S)
+    else s = (float)((double)acc[0][r] + (double)acc[1][r] + (double)acc[2][r]);   // exact sum, then RN32
     y[r] = __builtin_fmaf(s, c, 0.0f);               // +0 addend: a zero sum gives +0
   }
+}
+
+// Split packed bf16 pairs into up to three magnitude parts: below t2 goes
+// down a part, and of that, below t3 down another (both halves of each
+// threshold hold the same bf16 magnitude bits).
+template <int PARTS>
+__device__ __forceinline__ void split_parts(const uint4& v, uint32_t t2, uint32_t t3, uint4 (&part)[3]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[3][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (PARTS == 1) {
+      o[0][i] = w[i];
+    } else {
+      const uint32_t low = split_low(w[i], t2);
+      o[0][i] = w[i] ^ low;
+      if constexpr (PARTS == 2) {
+        o[1][i] = low;
+      } else {
+        const uint32_t lowest = split_low(low, t3);
+        o[1][i] = low ^ lowest;
+        o[2][i] = lowest;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PARTS; ++q) part[q] = uint4{o[q][0], o[q][1], o[q][2], o[q][3]};
 }
 
 // Element i of a block after the rotation, computed exactly from the bf16
@@ -462,11 +498,6 @@ __device__ __forceinline__ void issue_tile(const QuantParams& p, int64_t row0, i
   }
 }
 
-// Split two packed bf16 values into (high, low) parts when `two`.
-__device__ __forceinline__ void split_pair(uint32_t w, uint32_t t2, bool two, uint32_t& hi, uint32_t& lo) {
-  lo = two ? split_low(w, t2) : 0u;
-  hi = w ^ lo;
-}
 
 // Scale bytes of 8 consecutive blocks of a row, held by lanes 8a .. 8a+7
 // (k = lane % 8): with 8-byte aligned scale rows and all 8 blocks inside the
@@ -562,11 +593,93 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
   }
 }
 
+// Row and column passes of a tile on the matrix cores, with the inputs split
+// into PARTS magnitude parts (thresholds t2, t3).
+//   row pass: wave w, group g = the 32 blocks of rows 8w + 4g .. +3;
+//   column pass: wave w, group g = columns 64w + 32g .. +31.  A lane's
+//   operand (8 consecutive rows of its column) comes from two transposed LDS
+//   reads: in each 16-lane group, lane s reads 4 consecutive columns of row
+//   s / 4, and lane j receives column j of the 4 rows (ds_read_b64_tr_b16).
+template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL, int PARTS>
+__device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t* buf, int t, int64_t row0, int64_t col0,
+                                            const uint4* htab, uint32_t t2, uint32_t t3, bool wide_scales) {
+  const int lane = t & 63, wave = t >> 6, hl = lane >> 5, n = lane & 31;
+  const bf16x8 ha[2] = {__builtin_bit_cast(bf16x8, htab[2 * lane]), __builtin_bit_cast(bf16x8, htab[2 * lane + 1])};
+  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
+  if constexpr (DO_ROW) {
+    const bool full_width = col0 + kTileCols <= p.cols;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int r = 8 * wave + 4 * g + (n >> 3), k = n & 7;
+      uint4 part[3][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 v = *(const uint4*)(buf + r * kRowBytes +
+                                        lds_col(32 * k + 16 * h + 8 * hl, ((n >> 3) & 1) | ((wave & 1) << 3)));
+        uint4 ph[3];
+        split_parts<PARTS>(v, t2, t3, ph);
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) part[q][h] = ph[q];
+      }
+      float y[16];
+      mfma_block_sums<PARTS>(ha, part, c, y);
+      const int64_t row = row0 + r, c0 = col0 + 32 * k;
+      const bool valid = row < p.rows && c0 < p.cols;
+      uint32_t w[2];
+      const uint32_t byte = cast_half_block<GRID, ROUND>(
+          y, lane, (((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2) + 4 * hl, 0u, k0, k1, w);
+      if (valid) *(uint2*)(p.row_codes + row * p.ld_row_codes + c0 / 2 + 8 * hl) = uint2{w[0], w[1]};
+      store_row_scales(p.row_scales + row * p.ld_row_scales + col0 / 32, k, byte, wide_scales && full_width,
+                       valid && hl == 0);
+    }
+  }
+  if constexpr (DO_COL) {
+    const int g16 = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int col = 64 * wave + 32 * g + 16 * (g16 & 1) + 4 * (s & 3);    // this lane's source columns
+      uint4 part[3][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t d[4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int row = 16 * h + 8 * (g16 >> 1) + 4 * half + (s >> 2);
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          const v4s q = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) uint8_t*)lds_addr(buf) +
+                                                       row * kRowBytes + lds_col(col, row & 9)));
+          d[2 * half] = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
+          d[2 * half + 1] = (uint32_t)(uint16_t)q[2] | ((uint32_t)(uint16_t)q[3] << 16);
+        }
+        uint4 ph[3];
+        split_parts<PARTS>(uint4{d[0], d[1], d[2], d[3]}, t2, t3, ph);
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) part[q][h] = ph[q];
+      }
+      float y[16];
+      mfma_block_sums<PARTS>(ha, part, c, y);
+      const int64_t cc = col0 + 64 * wave + 32 * g + n;
+      uint32_t w[2];
+      const uint32_t byte = cast_half_block<GRID, ROUND>(
+          y, lane, (((uint64_t)cc * (uint64_t)p.rows + (uint64_t)row0) >> 2) + 4 * hl, 1u, k0, k1, w);
+      if (cc < p.cols) {
+        *(uint2*)(p.col_codes + cc * p.ld_col_codes + row0 / 2 + 8 * hl) = uint2{w[0], w[1]};
+        if (hl == 0) p.col_scales[cc * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
 template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(wgs_per_cu(ROUND))))
 quant_kernel(const QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kPartBytes];   // two tile buffers
   __shared__ uint32_t red[2 * (kThreads / 64)];
+  __shared__ uint4 htab[2 * 64];       // the sign-Hadamard MFMA operand of each lane (two K-halves)
 
   const int tid = threadIdx.x;
   const uint32_t xcd = blockIdx.x & 7u, J = gridDim.x >> 3;
@@ -574,11 +687,15 @@ quant_kernel(const QuantParams p) {
   int64_t row0 = 0, col0 = 0;
   if (!next_tile(p, xcd, J, tau, row0, col0)) return;
   issue_tile(p, row0, col0, tid >> 6, tid & 63, lds);
-  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
   const bool wide_scales = DO_ROW && ((((uintptr_t)p.row_scales) | (uintptr_t)p.ld_row_scales) & 7u) == 0;
-  const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
-  bf16x8 ha[2];
-  if constexpr (HAD > 0) hadamard_operand<HAD>(p.sign_mask, tid & 63, ha);
+  if constexpr (HAD > 0) {
+    if (tid < 64) {                    // read after the first barrier below
+      bf16x8 ha[2];
+      hadamard_operand<HAD>(p.sign_mask, tid, ha);
+      htab[2 * tid] = __builtin_bit_cast(uint4, ha[0]);
+      htab[2 * tid + 1] = __builtin_bit_cast(uint4, ha[1]);
+    }
+  }
   int cur = 0;
 
   for (;;) {
@@ -588,7 +705,7 @@ quant_kernel(const QuantParams p) {
     int t = tid;
     uint32_t mask = p.sign_mask;
     asm volatile("" : "+v"(t), "+v"(mask));
-    const int lane = t & 63, wave = t >> 6, hl = lane >> 5, n = lane & 31;
+    const int lane = t & 63, wave = t >> 6;
     uint8_t* buf = lds + cur * kPartBytes;
 
     // ---- 1. this tile has landed in LDS (every wave's copies), and every wave
@@ -632,7 +749,7 @@ quant_kernel(const QuantParams p) {
 
     // ---- 3. classify by the exponent fields of the largest and smallest nonzero |x|
     int cls = kClsMfma1;
-    uint32_t t2 = 0;                                // split threshold (both halves)
+    uint32_t t2 = 0, t3 = 0;                        // split thresholds (both halves)
     if (mx >= (250u << 7)) {
       cls = kClsSpecial;                            // Inf/NaN or sums that could overflow
     } else if (HAD > 0 && mn != 0xFFFFu) {
@@ -640,83 +757,21 @@ quant_kernel(const QuantParams p) {
       const int fmin = max((int)((mn + 1u) >> 7), 1);
       const int span = fmax - fmin;
       if (span > 40) cls = kClsSpecial;
-      else if (fmin < 8 || span > 23) cls = kClsF64;
+      else if (fmin < 8 || span > 35) cls = kClsF64;
       else if (span > 11) {
-        cls = kClsMfma2;
+        cls = span > 23 ? kClsMfma3 : kClsMfma2;
         t2 = (uint32_t)(fmax - 11) << 7;
         t2 |= t2 << 16;
+        t3 = (uint32_t)(fmax - 23) << 7;
+        t3 |= t3 << 16;
       }
     }
 
-    const bool full_width = col0 + kTileCols <= p.cols;
-    if (HAD > 0 && (cls == kClsMfma1 || cls == kClsMfma2)) {
+    if (HAD > 0 && cls <= kClsMfma3) {
       if constexpr (HAD > 0) {
-        const bool two = cls == kClsMfma2;
-        // ---- 4a. row pass on the matrix cores: wave w, group g = blocks of
-        // rows 8w + 4g .. +3 (8 blocks per row)
-        if constexpr (DO_ROW) {
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int r = 8 * wave + 4 * g + (n >> 3), k = n & 7;
-            uint4 bh[2], bl[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const uint4 v = *(const uint4*)(buf + r * kRowBytes +
-                                              lds_col(32 * k + 16 * h + 8 * hl, ((n >> 3) & 1) | ((wave & 1) << 3)));
-              split_pair(v.x, t2, two, bh[h].x, bl[h].x);
-              split_pair(v.y, t2, two, bh[h].y, bl[h].y);
-              split_pair(v.z, t2, two, bh[h].z, bl[h].z);
-              split_pair(v.w, t2, two, bh[h].w, bl[h].w);
-            }
-            float y[16];
-            if (two) mfma_block_sums<true>(ha, bh, bl, c, y);
-            else mfma_block_sums<false>(ha, bh, bl, c, y);
-            const int64_t row = row0 + r, c0 = col0 + 32 * k;
-            const bool valid = row < p.rows && c0 < p.cols;
-            uint32_t w[2];
-            const uint32_t byte = cast_half_block<GRID, ROUND>(
-                y, lane, (((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2) + 4 * hl, 0u, k0, k1, w);
-            if (valid) *(uint2*)(p.row_codes + row * p.ld_row_codes + c0 / 2 + 8 * hl) = uint2{w[0], w[1]};
-            store_row_scales(p.row_scales + row * p.ld_row_scales + col0 / 32, k, byte, wide_scales && full_width,
-                             valid && hl == 0);
-          }
-        }
-        // ---- 4b. column pass on the matrix cores: wave w, group g = columns
-        // 64w + 32g .. +31
-        if constexpr (DO_COL) {
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int cc = 64 * wave + 32 * g + n;
-            const uint32_t cb0 = lds_col(cc, hl << 3), cb1 = lds_col(cc, (hl << 3) | 1);
-            uint4 bh[2], bl[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              uint32_t vh[4], vl[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int j = 16 * h + 8 * hl + 2 * e;
-                const uint32_t v = (uint32_t)*(const uint16_t*)(buf + j * kRowBytes + cb0) |
-                                   ((uint32_t)*(const uint16_t*)(buf + (j + 1) * kRowBytes + cb1) << 16);
-                split_pair(v, t2, two, vh[e], vl[e]);
-              }
-              bh[h] = uint4{vh[0], vh[1], vh[2], vh[3]};
-              bl[h] = uint4{vl[0], vl[1], vl[2], vl[3]};
-            }
-            float y[16];
-            if (two) mfma_block_sums<true>(ha, bh, bl, c, y);
-            else mfma_block_sums<false>(ha, bh, bl, c, y);
-            const int64_t col = col0 + cc;
-            uint32_t w[2];
-            const uint32_t byte = cast_half_block<GRID, ROUND>(
-                y, lane, (((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2) + 4 * hl, 1u, k0, k1, w);
-            if (col < p.cols) {
-              *(uint2*)(p.col_codes + col * p.ld_col_codes + row0 / 2 + 8 * hl) = uint2{w[0], w[1]};
-              if (hl == 0) p.col_scales[col * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
-            }
-          }
-        }
+        if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+        else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+        else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
       }
     } else {
       // ---- 4c. no rotation, float64 butterflies or exact fixed point: each
@@ -765,7 +820,7 @@ hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int r
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  const int64_t wgs_per_xcd = std::max<int64_t>(1, (int64_t)cus * kWgPerCu / 8);
+  const int64_t wgs_per_xcd = std::max<int64_t>(1, (int64_t)cus * wgs_per_cu(round) / 8);
   const dim3 g((unsigned)(8 * std::min(per_xcd, wgs_per_xcd)));
   if (!rht) p.sign_mask = 0u;
   if (had_n == 0) return launch_cast<0>(p, grid_kind, round, do_row, do_col, g, s);

@@ -28,8 +28,9 @@ design notes):
 * RTNE: nearest level, a tie goes to the even code, anything above the top
   level saturates to it;
 * SR: with lo <= v < hi adjacent levels, frac = (v - lo) / (hi - lo) and
-  P = floor(frac * 2^32), the magnitude rounds up iff u < P for the element's
-  32-bit Philox word u; v at or above the top level saturates;
+  P = floor(frac * 2^22), the magnitude rounds up iff P + floor(u / 2^10) >= 2^22
+  for the element's 32-bit Philox word u, i.e. floor(frac + r) with r the top
+  22 bits of u read as a fraction; v at or above the top level saturates;
 * the Philox word of the element at index i of the output's logical row-major
   order (row r, column c of a row-wise output: i = r*cols + c; a column-wise
   output is indexed in the transposed tensor: i = c*rows + r) is word i mod 4
@@ -65,6 +66,13 @@ def rtne_magnitude_codes(v, grid):
 def sr_magnitude_codes(v, u, grid):
     """Stochastic rounding of v >= 0 onto the grid, given 32-bit words u (same shape).
 
+    Round up from the largest level lo <= v iff floor(frac * 2^22) + (u >> 10)
+    >= 2^22: frac = (v - lo) / (hi - lo) truncated to 22 bits, plus a 22-bit
+    uniform fraction (the top bits of u), carried into the integer part.  The
+    probability of rounding up is floor(frac * 2^22) / 2^22, so E[SR(v)] = v up
+    to less than 2^-22 of a step ("Résumé Technique : TetraJet-v2", section 2:
+    unbiased stochastic rounding).
+
     v - lo is exact in float64: either lo = 0, or lo >= v/2 (Sterbenz), since
     adjacent levels of both grids are at most a factor 2 apart.
     """
@@ -74,8 +82,9 @@ def sr_magnitude_codes(v, u, grid):
     lo_c = np.minimum(lo, len(lv) - 2)
     width = lv[lo_c + 1] - lv[lo_c]
     frac = (v - lv[lo_c]) / width                   # width is a power of two: exact
-    p = np.floor(frac * 2.0 ** 32)                  # 32-bit fixed-point probability
-    up = np.asarray(u, dtype=np.float64) < p
+    p22 = np.floor(frac * 2.0 ** 22)                # 22-bit fixed-point probability
+    r22 = (np.asarray(u, dtype=np.uint64) >> np.uint64(10)).astype(np.float64)
+    up = p22 + r22 >= 2.0 ** 22
     code = np.where(top, len(lv) - 1, lo + up.astype(np.int64))
     return code.astype(np.uint8)
 
@@ -179,8 +188,8 @@ def cast_scalar(v, grid, rounding, u=0):
     """Magnitude code of one exact value v >= 0 (a Fraction), by exhaustive search.
 
     RTNE: the level nearest to v; on a tie the even code.  SR: round up from
-    the largest level <= v iff u < floor(frac * 2^32).  Above the top level
-    both saturate.
+    the largest level <= v iff floor(frac * 2^22) + (u >> 10) >= 2^22.  Above
+    the top level both saturate.
     """
     lv = [Fraction(x) for x in levels(grid)]
     v = Fraction(v)
@@ -191,5 +200,5 @@ def cast_scalar(v, grid, rounding, u=0):
         return best
     lo = max(k for k in range(len(lv)) if lv[k] <= v)
     frac = (v - lv[lo]) / (lv[lo + 1] - lv[lo])
-    p = (frac * 2 ** 32).numerator // (frac * 2 ** 32).denominator
-    return lo + (1 if u < p else 0)
+    p22 = (frac * 2 ** 22).numerator // (frac * 2 ** 22).denominator
+    return lo + (1 if p22 + (int(u) >> 10) >= 2 ** 22 else 0)

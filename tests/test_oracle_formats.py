@@ -157,12 +157,20 @@ def test_sr_array_matches_scalar(grid):
 
 
 def test_sr_threshold_is_floor_of_fixed_point_probability():
-    # frac = 1/3 cannot be held in 32 bits; P = floor(2^32/3) = 1431655765
-    v = np.array([0.5 + 0.5 / 3])      # float64 rounding of 2/3 keeps P's floor value
-    p = int(np.floor((v[0] - 0.5) / 0.5 * 2 ** 32))
-    assert sr_magnitude_codes(v, np.array([p - 1]), F.E2M1)[0] == 2
-    assert sr_magnitude_codes(v, np.array([p]), F.E2M1)[0] == 1
-    assert sr_magnitude_codes(np.array([1.0]), np.array([0]), F.E2M1)[0] == 2   # on a level: unchanged
+    # frac = 1/3 cannot be held in 22 bits: P22 = floor(2^22 / 3) = 1398101, and v rounds up iff the top 22
+    # bits of u reach 2^22 - P22 = 2796203
+    v = np.array([0.5 + 0.5 / 3])      # float64 rounding of 2/3 keeps P22's floor value
+    assert int(np.floor((v[0] - 0.5) / 0.5 * 2 ** 22)) == 1398101
+    edge = 2796203 << 10
+    assert sr_magnitude_codes(v, np.array([edge]), F.E2M1)[0] == 2
+    assert sr_magnitude_codes(v, np.array([edge + 1023]), F.E2M1)[0] == 2
+    assert sr_magnitude_codes(v, np.array([edge - 1]), F.E2M1)[0] == 1
+    assert sr_magnitude_codes(v, np.array([0]), F.E2M1)[0] == 1
+    assert sr_magnitude_codes(np.array([1.0]), np.array([0xFFFFFFFF]), F.E2M1)[0] == 2   # on a level: unchanged
+    # the probability is the 22-bit truncated fraction: exactly P22 of the 2^22 values of u >> 10 round up
+    r = np.arange(0, 2 ** 22, 97, dtype=np.uint64) << np.uint64(10)
+    ups = sr_magnitude_codes(np.full(r.shape, v[0]), r, F.E2M1) == 2
+    assert ups.sum() == np.count_nonzero((r >> np.uint64(10)) >= 2796203)
 
 
 # ---- exact fp32 rounding of wide sums ------------------------------------------
