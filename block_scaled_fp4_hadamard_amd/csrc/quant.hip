@@ -28,8 +28,12 @@
 // binades take a third part; the three exact fp32 sums then add exactly in
 // float64 (at most 48 significant bits) before the one rounding to fp32.
 // Wider tiles (and tiles with values below 2^-119, whose partial sums could be
-// subnormal) take float64 butterflies, exact up to a 40-binade span;
-// non-finite, near-overflow and wider tiles take an exact fixed-point path.
+// subnormal) take float64 butterflies, exact up to a 40-binade span.  Tiles
+// that are wider still, or hold non-finite or near-overflow values, take the
+// same butterflies for every block; then each block that on its own is that
+// wide or holds such a value is redone exactly by the whole workgroup, one
+// output per thread, in fixed point (a few such blocks cost a few
+// microseconds, not the tile's whole fixed-point work on 256 lanes).
 //
 // The E2M1 casts use gfx950's scaled fp4 conversions, which divide by the
 // power-of-two scale given as a float and saturate: ties to even for RTNE,
@@ -76,7 +80,7 @@ constexpr int kClsMfma1 = 0;     // matrix-core sums, one part (or no rotation)
 constexpr int kClsMfma2 = 1;     // matrix-core sums, high + low parts
 constexpr int kClsMfma3 = 2;     // matrix-core sums, high + middle + low parts
 constexpr int kClsF64 = 3;       // float64 butterflies
-constexpr int kClsSpecial = 4;   // exact fixed point, careful casting
+constexpr int kClsSpecial = 4;   // float64 butterflies, then an exact redo of the blocks that need it
 
 __device__ __forceinline__ uint32_t e8m0_scale_bits(uint32_t byte) {
   // the float whose exponent the scaled conversions divide by: 2^(byte-127)
@@ -406,36 +410,87 @@ __device__ __forceinline__ float special_value(Get get, int i, uint32_t mask) {
   }
 }
 
-// One block of a tile that needs the exact rotation or careful casting
-// (non-finite, near-overflow or very wide inputs): element by element, every
-// y computed twice (once for the block maximum, once to cast), so that
-// nothing here needs private arrays.  A block with a non-finite y gets scale
-// 0xFF and zero codes.
-template <int HAD, int GRID, int ROUND, typename Get>
-__device__ __forceinline__ void special_block(Get get, uint32_t mask, uint64_t ctr, uint32_t stream, uint32_t k0,
-                                              uint32_t k1, uint8_t* codes, uint8_t* scale) {
-  uint32_t mb = 0;
-#pragma unroll 1
-  for (int i = 0; i < 32; ++i) mb = max(mb, __float_as_uint(special_value<HAD>(get, i, mask)) & 0x7FFFFFFFu);
-  if (mb >= 0x7F800000u) {
-    *(uint4*)codes = uint4{0u, 0u, 0u, 0u};
-    *scale = 0xFFu;
-    return;
+// Whether the block of 32 bf16 inputs get(j) must be redone exactly after the
+// float64 butterflies: with rotation, when an input is Inf or NaN or has
+// |x| >= 2^123 (the fp32 sum could overflow), or when the largest and the
+// smallest nonzero |x| lie more than 40 binades apart (subnormals counted as
+// exponent field 1); without rotation, when an input is Inf or NaN.
+template <int HAD, typename Get>
+__device__ __forceinline__ bool block_needs_exact(Get get) {
+  uint32_t mx = 0, mn = 0xFFFFu;
+#pragma unroll 8
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t m = get(j) & 0x7FFFu;
+    mx = max(mx, m);
+    if (m != 0u) mn = min(mn, m);
   }
-  const uint32_t byte = scale_byte<GRID>(mb >> 23);
-#pragma unroll 1
-  for (int g = 0; g < 8; ++g) {                 // 4 elements: one Philox block
-    U4 r = {0u, 0u, 0u, 0u};
-    if constexpr (ROUND == MX_ROUND_SR)
-      r = philox4x32_10((uint32_t)(ctr + g), (uint32_t)((ctr + g) >> 32), stream, 0u, k0, k1);
-    uint32_t half = 0;
-    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 0, mask), byte, r.x);
-    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 1, mask), byte, r.y) << 4;
-    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 2, mask), byte, r.z) << 8;
-    half |= cast_one<GRID, ROUND>(special_value<HAD>(get, 4 * g + 3, mask), byte, r.w) << 12;
-    *(uint16_t*)(codes + 2 * g) = (uint16_t)half;
+  if constexpr (HAD == 0) {
+    return mx >= 0x7F80u;
+  } else {
+    if (mx >= (250u << 7)) return true;
+    if (mn == 0xFFFFu) return false;
+    return max((int)(mx >> 7), 1) - max((int)(mn >> 7), 1) > 40;
   }
-  *scale = (uint8_t)byte;
+}
+
+// Exact redo of the n blocks listed in fix[]: entry = axis << 15 | owner,
+// owner being the lane that holds the block in the float64 passes (row pass:
+// 8 r + k for chunk k of tile row r; column pass: the tile column).  In round
+// c, thread t computes output t % 32 of entry c + t / 32 in fixed point, so a
+// block's 32 outputs meet in one half wave: the block maximum and the code
+// words are gathered there.  A block with a non-finite output gets scale 0xFF
+// and zero codes.  n is the same in every thread.
+template <int HAD, int GRID, int ROUND>
+__device__ __forceinline__ void exact_fixup(const QuantParams& p, const uint8_t* buf, int t, int64_t row0,
+                                            int64_t col0, uint32_t mask, const uint16_t* fix, int n) {
+  const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  const int i = t & 31;
+#pragma unroll 1
+  for (int c = 0; c < n; c += kThreads / 32) {
+    const int e = c + (t >> 5);
+    const bool active = e < n;
+    const uint32_t ent = active ? (uint32_t)fix[e] : 0u;
+    const bool col_axis = (ent >> 15) != 0u;
+    const int owner = (int)(ent & 0x7FFFu);
+    float y;
+    uint64_t ctr;
+    uint8_t* codes;
+    uint8_t* scale;
+    if (col_axis) {
+      y = special_value<HAD>([&](int j) { return (uint32_t)*(const uint16_t*)(buf + lds_off(j, owner)); }, i, mask);
+      const int64_t col = col0 + owner;
+      ctr = ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2;
+      codes = p.col_codes + col * p.ld_col_codes + row0 / 2;
+      scale = p.col_scales + col * p.ld_col_scales + row0 / 32;
+    } else {
+      const int r = owner >> 3, k = owner & 7;
+      y = special_value<HAD>([&](int j) { return (uint32_t)*(const uint16_t*)(buf + lds_off(r, 32 * k + j)); }, i,
+                             mask);
+      const int64_t row = row0 + r, c0 = col0 + 32 * k;
+      ctr = ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2;
+      codes = p.row_codes + row * p.ld_row_codes + c0 / 2;
+      scale = p.row_scales + row * p.ld_row_scales + c0 / 32;
+    }
+    uint32_t mb = __float_as_uint(y) & 0x7FFFFFFFu;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+    const bool nonfinite = mb >= 0x7F800000u;
+    const uint32_t byte = nonfinite ? 0xFFu : scale_byte<GRID>(mb >> 23);
+    uint32_t u = 0;
+    if constexpr (ROUND == MX_ROUND_SR) {
+      const uint64_t g = ctr + (uint64_t)(i >> 2);     // element i draws word i % 4 of block ctr + i / 4
+      const U4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), col_axis ? 1u : 0u, 0u, k0, k1);
+      u = (i & 2) ? ((i & 1) ? r.w : r.z) : ((i & 1) ? r.y : r.x);
+    }
+    uint32_t word = nonfinite ? 0u : cast_one<GRID, ROUND>(y, byte, u) << (4 * (i & 7));
+    word |= (uint32_t)__shfl_xor((int)word, 1);
+    word |= (uint32_t)__shfl_xor((int)word, 2);
+    word |= (uint32_t)__shfl_xor((int)word, 4);
+    if (active) {
+      if ((i & 7) == 0) *(uint32_t*)(codes + 4 * (i >> 3)) = word;
+      if (i == 0) *scale = (uint8_t)byte;
+    }
+  }
 }
 
 // Tile walk: workgroup (xcd, j) of J per XCD takes the XCD's tile sequence
@@ -516,15 +571,18 @@ __device__ __forceinline__ void store_row_scales(uint8_t* dst, int k, uint32_t b
   }
 }
 
-// Passes in which each lane reads a whole block: no rotation, float64
-// butterflies (kClsF64) or the exact fixed-point path (kClsSpecial).  Row
-// pass: lane (r, k) owns chunk k of row r; column pass: lane c owns column c.
+// Passes in which each lane reads a whole block: no rotation or float64
+// butterflies.  Row pass: lane (r, k) owns chunk k of row r; column pass:
+// lane c owns column c.  In a kClsSpecial tile the blocks that the
+// butterflies may get wrong are then listed in fix[] (count *fix_n, zero on
+// entry and on return) and redone exactly.
 template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
 __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const uint8_t* hi_part, int t, int64_t row0,
-                                                  int64_t col0, int cls, uint32_t mask, bool wide_scales) {
+                                                  int64_t col0, int cls, uint32_t mask, bool wide_scales,
+                                                  uint16_t* fix, uint32_t* fix_n) {
   const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
   const bool full_width = col0 + kTileCols <= p.cols;
-  if (cls != kClsSpecial) {
+  {
     if constexpr (DO_ROW) {
       const int r = t >> 3, k = t & 7;
       const int64_t row = row0 + r, c0 = col0 + 32 * k;
@@ -572,25 +630,29 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
         p.col_scales[col * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
       }
     }
-  } else {
-    if constexpr (DO_ROW) {
-      const int r = t >> 3, k = t & 7;
-      const int64_t row = row0 + r, c0 = col0 + 32 * k;
-      if (row < p.rows && c0 < p.cols)
-        special_block<HAD, GRID, ROUND>(
-            [&](int j) { return (uint32_t)*(const uint16_t*)(hi_part + lds_off(r, 32 * k + j)); }, mask,
-            ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2, 0u, k0, k1,
-            p.row_codes + row * p.ld_row_codes + c0 / 2, p.row_scales + row * p.ld_row_scales + c0 / 32);
-    }
-    if constexpr (DO_COL) {
-      const int64_t col = col0 + t;
-      if (col < p.cols)
-        special_block<HAD, GRID, ROUND>(
-            [&](int j) { return (uint32_t)*(const uint16_t*)(hi_part + lds_off(j, t)); }, mask,
-            ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2, 1u, k0, k1,
-            p.col_codes + col * p.ld_col_codes + row0 / 2, p.col_scales + col * p.ld_col_scales + row0 / 32);
-    }
   }
+  if (cls != kClsSpecial) return;
+  // ---- list the blocks to redo, then redo them (all threads: the count and
+  // the barriers are workgroup-uniform)
+  if constexpr (DO_ROW) {
+    const int r = t >> 3, k = t & 7;
+    if (row0 + r < p.rows && col0 + 32 * k < p.cols &&
+        block_needs_exact<HAD>([&](int j) { return (uint32_t)*(const uint16_t*)(hi_part + lds_off(r, 32 * k + j)); }))
+      fix[atomicAdd(fix_n, 1u)] = (uint16_t)t;
+  }
+  if constexpr (DO_COL) {
+    if (col0 + t < p.cols &&
+        block_needs_exact<HAD>([&](int j) { return (uint32_t)*(const uint16_t*)(hi_part + lds_off(j, t)); }))
+      fix[atomicAdd(fix_n, 1u)] = (uint16_t)(0x8000 | t);
+  }
+  // the butterflies' stores of these blocks are complete before they are
+  // overwritten, and the list is whole
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int n = (int)*(volatile uint32_t*)fix_n;
+  __syncthreads();
+  if (t == 0) *fix_n = 0u;
+  if (n > 0) exact_fixup<HAD, GRID, ROUND>(p, hi_part, t, row0, col0, mask, fix, n);
 }
 
 // Row and column passes of a tile on the matrix cores, with the inputs split
@@ -680,6 +742,8 @@ quant_kernel(const QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kPartBytes];   // two tile buffers
   __shared__ uint32_t red[2 * (kThreads / 64)];
   __shared__ uint4 htab[2 * 64];       // the sign-Hadamard MFMA operand of each lane (two K-halves)
+  __shared__ uint16_t fix[2 * kThreads];   // blocks of a kClsSpecial tile to redo exactly
+  __shared__ uint32_t fix_n;
 
   const int tid = threadIdx.x;
   const uint32_t xcd = blockIdx.x & 7u, J = gridDim.x >> 3;
@@ -696,6 +760,7 @@ quant_kernel(const QuantParams p) {
       htab[2 * tid + 1] = __builtin_bit_cast(uint4, ha[1]);
     }
   }
+  if (tid == 0) fix_n = 0u;            // read after the first barrier below
   int cur = 0;
 
   for (;;) {
@@ -776,7 +841,7 @@ quant_kernel(const QuantParams p) {
     } else {
       // ---- 4c. no rotation, float64 butterflies or exact fixed point: each
       // lane casts whole blocks
-      lane_block_passes<HAD, GRID, ROUND, DO_ROW, DO_COL>(p, buf, t, row0, col0, cls, mask, wide_scales);
+      lane_block_passes<HAD, GRID, ROUND, DO_ROW, DO_COL>(p, buf, t, row0, col0, cls, mask, wide_scales, fix, &fix_n);
     }
     if (!more) break;
     tau = tau_next;

@@ -122,6 +122,42 @@ def test_exact_sum_boundaries(had_n, had_kind, signs):
     check(bits, "spans-sr", axis="both", had_n=had_n, had_kind=had_kind, had_seed=4, rounding="sr", seed=8)
 
 
+def wide_tile_tensor():
+    """96 x 512 Laplace values around 2^-10: tiles that span more than 40 binades as a whole but in few or
+    none of their blocks.  Tile (0,0): one tiny value (2^-60), so its row block and column block span ~50
+    binades.  Tile (0,1): a spike of 2^20 in one block and a value of 2^-25 in another, so the tile spans
+    48 binades and no block more than 40.  Tile (1,0): 24 tiny values scattered over rows and columns (one
+    row or column block may hold two).  Tile (2,1): the same with a tiny value in every 32nd column and one
+    Inf.  The rest are ordinary tiles."""
+    rng = np.random.default_rng(31)
+    x = rng.laplace(0.0, 2.0 ** -10, (96, 512)).astype(np.float32)
+    x[7, 100] = np.float32(2.0 ** -60)
+    x[3, 300] = np.float32(2.0 ** 20)
+    x[20, 400] = np.float32(-(2.0 ** -25))
+    rr = rng.integers(32, 64, 24)
+    cc = rng.integers(0, 256, 24)
+    x[rr, cc] = (np.exp2(rng.integers(-90, -55, 24)) * rng.choice([-1.0, 1.0], 24)).astype(np.float32)
+    for c in range(256, 512, 32):
+        x[64 + (c // 32) % 32, c + 5] = np.float32(2.0 ** -70)
+    bits = synth.f32_to_bf16_bits(x)
+    bits[70, 333] = 0x7F80
+    return bits
+
+
+@pytest.mark.parametrize("had_n,had_kind", [(16, "det"), (32, "rand")])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_wide_tiles_with_few_wide_blocks(had_n, had_kind, rounding):
+    """Tiles wider than 40 binades take float64 butterflies and then redo only the blocks that need it."""
+    bits = wide_tile_tensor()
+    for grid in ("e2m1", "e1m2"):
+        check(bits, "wide-tiles", axis="both", grid=grid, rounding=rounding, seed=13, had_n=had_n,
+              had_kind=had_kind, had_seed=77)
+    check(bits, "wide-tiles-row", axis="row", rounding=rounding, seed=13, had_n=had_n, had_kind=had_kind,
+          had_seed=77)
+    check(bits, "wide-tiles-col", axis="col", rounding=rounding, seed=13, had_n=had_n, had_kind=had_kind,
+          had_seed=77)
+
+
 def test_repeatable():
     bits = synth.activation(64, 512, np.random.default_rng(1))
     x = to_gpu_bits(bits)
