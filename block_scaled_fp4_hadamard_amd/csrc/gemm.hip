@@ -168,6 +168,66 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, int64_t row0, in
     }
 }
 
+// Whole-tile epilogue with wide stores.  For each group of four accumulator
+// registers (four consecutive rows) and each quad of lanes (four consecutive
+// columns) the 4x4 block is transposed with two DPP exchanges (lane pairs
+// l ^ 1, then l ^ 2), after which lane 4a + k holds row k of the block,
+// columns 4a .. 4a + 3 in order: one 16-byte (fp32) or 8-byte (bf16) store
+// per lane and register group, every row segment a whole 128- or 64-byte
+// run.  Values are moved, never combined, so the stored numbers are the
+// accumulators' bit for bit.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+}
+
+__device__ __forceinline__ void transpose4(float (&v)[4], int lane) {
+  const bool odd = (lane & 1) != 0, hi = (lane & 2) != 0;
+  // pairs (0,1), (2,3) across lanes l, l ^ 1
+#pragma unroll
+  for (int r = 0; r < 4; r += 2) {
+    const float got = dpp_xor1(odd ? v[r] : v[r + 1]);
+    if (odd) v[r] = got;
+    else v[r + 1] = got;
+  }
+  // pairs (0,2), (1,3) across lanes l, l ^ 2
+  const float g0 = dpp_xor2(hi ? v[0] : v[2]);
+  const float g1 = dpp_xor2(hi ? v[1] : v[3]);
+  if (hi) {
+    v[0] = g0;
+    v[1] = g1;
+  } else {
+    v[2] = g0;
+    v[3] = g1;
+  }
+}
+
+template <int OUT, int MT, int NT>
+__device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row0, int64_t col0, int lane,
+                                                const v16f (&acc)[MT][NT]) {
+  const int half = lane >> 5, quad = (lane & 31) >> 2, k = lane & 3;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        transpose4(v, lane);
+        const int64_t row = row0 + i * 32 + 8 * g + 4 * half + k;
+        const int64_t col = col0 + j * 32 + 4 * quad;
+        if constexpr (OUT == MX_OUT_F32) {
+          *(float4*)((float*)p.c + row * p.ldc + col) = float4{v[0], v[1], v[2], v[3]};
+        } else {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          *(uint2*)((uint16_t*)p.c + row * p.ldc + col) = uint2{lo, hi2};
+        }
+      }
+}
+
 // Global -> LDS DMA of 16 (or 4) bytes per lane: LDS address = M0 + size*lane.
 // Issued as inline asm so the compiler does not place its own conservative
 // vmcnt waits for them; the kernel waits explicitly.  The instruction writes
@@ -312,40 +372,51 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   const int r0 = wm * 128, c0 = wn * 64;
   const int nk = (int)(p.K / 256);
 
-  // DMA: one instruction moves 64 lanes x 16 B = 1 KB = 8 rows of 128 B; wave w
-  // covers rows 32w .. 32w+31 in 4 instructions; lane i -> row +i/8, LDS slot
-  // i%8, which must hold global piece (i%8) ^ ((row>>1)&7).  Offsets are from
-  // the tile's first row (operands are < 4 GiB).
-  uint32_t oa[4], ob[4];
+  // DMA: one instruction moves 64 lanes x 16 B = 1 KB = 8 rows of 128 B; lane
+  // i -> row +i/8, LDS slot i%8, which must hold global piece (i%8) ^
+  // ((row>>1)&7).  Half the waves move a whole K step: waves w and w ^ 4
+  // (placed on one SIMD by the round-robin wave dispatch) take alternate
+  // steps, so that while one issues the step's 20 copies the other keeps that
+  // SIMD's matrix core busy; all eight issuing at once after the barrier
+  // stalled every SIMD behind the copies.  The
+  // wave covers rows 32(w & 3) + 128h .. +31 of A and of B (h = 0, 1), and
+  // the scale dwords of rows 64(w & 3) + lane of both.  Offsets are from the
+  // tile's first row (operands are < 4 GiB).
+  uint32_t oa[8], ob[8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int row = 32 * wave + 8 * c + (lane >> 3);
-    const int piece = (lane & 7) ^ ((row >> 1) & 7);
-    oa[c] = (uint32_t)(row * p.lda_codes + piece * 16);
-    ob[c] = (uint32_t)(row * p.ldb_codes + piece * 16);
-  }
-  // scales: 8 bytes per row per step as two dwords; waves 0-3 carry A (rows
-  // 64(w&3) + lane), waves 4-7 carry B
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int row = 32 * (wave & 3) + 128 * h + 8 * c + (lane >> 3);
+      const int piece = (lane & 7) ^ ((row >> 1) & 7);
+      oa[4 * h + c] = (uint32_t)(row * p.lda_codes + piece * 16);
+      ob[4 * h + c] = (uint32_t)(row * p.ldb_codes + piece * 16);
+    }
   const int srow = 64 * (wave & 3) + lane;
-  const bool s_is_a = wave < 4;
-  const uint32_t os = (uint32_t)(srow * (s_is_a ? p.lda_scales : p.ldb_scales));
-  const uint32_t lA = lds_addr(&sA[0][32 * wave * kRowBytes]), lB = lds_addr(&sB[0][32 * wave * kRowBytes]);
-  const uint32_t lS = s_is_a ? lds_addr(&sSA[0][64 * (wave & 3)]) : lds_addr(&sSB[0][64 * (wave & 3)]);
+  const uint32_t osa = (uint32_t)(srow * p.lda_scales), osb = (uint32_t)(srow * p.ldb_scales);
+  const uint32_t lA = lds_addr(&sA[0][32 * (wave & 3) * kRowBytes]), lB = lds_addr(&sB[0][32 * (wave & 3) * kRowBytes]);
+  const uint32_t lSA = lds_addr(&sSA[0][64 * (wave & 3)]), lSB = lds_addr(&sSB[0][64 * (wave & 3)]);
 
-  // DMA of K step kt of tile (tbm, tbn) into stage st
+  // DMA of K step kt of tile (tbm, tbn) into stage st, by the waves of parity kt % 2
   auto issue = [&](int tbm, int tbn, int kt, int st) {
+    if ((wave >> 2) != (kt & 1)) return;
     const int64_t m0 = (int64_t)tbm * kBM, n0 = (int64_t)tbn * kBN;
     const uint8_t* abase = wave_uniform(p.a_codes + m0 * p.lda_codes);
     const uint8_t* bbase = wave_uniform(p.b_codes + n0 * p.ldb_codes);
-    const uint8_t* sbase = wave_uniform(s_is_a ? p.a_scales + m0 * p.lda_scales : p.b_scales + n0 * p.ldb_scales);
+    const uint8_t* sabase = wave_uniform(p.a_scales + m0 * p.lda_scales);
+    const uint8_t* sbbase = wave_uniform(p.b_scales + n0 * p.ldb_scales);
     const uint32_t kb = (uint32_t)kt * kRowBytes;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      dma16_off(abase, oa[c] + kb, lA + st * kFullStageBytes + c * 8 * kRowBytes);
-      dma16_off(bbase, ob[c] + kb, lB + st * kFullStageBytes + c * 8 * kRowBytes);
-    }
-    dma4_off(sbase, os + 8 * kt, lS + st * (2 * kBM * 4));
-    dma4_off(sbase, os + 8 * kt + 4, lS + st * (2 * kBM * 4) + kBM * 4);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dma16_off(abase, oa[4 * h + c] + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+        dma16_off(bbase, ob[4 * h + c] + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+      }
+    dma4_off(sabase, osa + 8 * kt, lSA + st * (2 * kBM * 4));
+    dma4_off(sabase, osa + 8 * kt + 4, lSA + st * (2 * kBM * 4) + kBM * 4);
+    dma4_off(sbbase, osb + 8 * kt, lSB + st * (2 * kBN * 4));
+    dma4_off(sbbase, osb + 8 * kt + 4, lSB + st * (2 * kBN * 4) + kBN * 4);
   };
 
   v16f acc[4][2];
@@ -404,7 +475,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       mfma_quarter<GRID, 2>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile<OUT, false, 4, 2>(p, (int64_t)bm * kBM + r0, (int64_t)bn * kBN + c0, lane, acc);
+    store_tile_wide<OUT, 4, 2>(p, (int64_t)bm * kBM + r0, (int64_t)bn * kBN + c0, lane, acc);
     if (rn >= w.rounds) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -500,11 +571,13 @@ hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStre
   tm.groups = tm.groups_m * groups_n;
   const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
   const dim3 g((unsigned)wgs);
-  // the DMA path needs whole tiles, whole 256-element K steps (at least two) and
-  // 4-byte aligned scale rows
+  // the DMA path needs whole tiles, whole 256-element K steps (at least two),
+  // 4-byte aligned scale rows and output rows aligned for its 16-byte (fp32)
+  // or 8-byte (bf16) stores
   const bool full = (p.M % kBM == 0) && (p.N % kBN == 0) && (p.K % 256 == 0) && (p.K >= 512) &&
                     ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.b_scales % 4 == 0) &&
-                    (p.lda_scales % 4 == 0) && (p.ldb_scales % 4 == 0);
+                    (p.lda_scales % 4 == 0) && (p.ldb_scales % 4 == 0) &&
+                    (p.ldc % 4 == 0) && ((uintptr_t)p.c % (out_kind == MX_OUT_F32 ? 16 : 8) == 0);
   if (grid_kind == MX_GRID_E2M1) {
     if (out_kind == MX_OUT_F32) launch_kind<MX_GRID_E2M1, MX_OUT_F32>(p, tm, full, g, s);
     else launch_kind<MX_GRID_E2M1, MX_OUT_BF16>(p, tm, full, g, s);

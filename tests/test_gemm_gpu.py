@@ -52,6 +52,23 @@ def test_gemm_bf16_output_is_rounded_fp32():
     assert_gemm_close(c16, c_ref, g, "bf16", bf16=True)
 
 
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("m,n,k", [(768, 512, 1024), (512, 1280, 2048)])
+def test_whole_tile_path_both_outputs(grid, m, n, k):
+    """Shapes on the DMA-pipelined whole-tile path (several tiles per workgroup round, several K steps):
+    fp32 against the oracle, bf16 equal to the RNE cast of the fp32 result element for element."""
+    announce("gemm whole-tile %s %dx%dx%d" % (grid, m, n, k))
+    rng = np.random.default_rng(m + n + k)
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c32 = run_gemm(a, b, grid, torch.float32)
+    c16 = run_gemm(a, b, grid, torch.bfloat16)
+    c_ref, g = gemm_ref(*a, *b, k, grid)
+    assert_gemm_close(c32, c_ref, g, "whole-tile fp32 %s" % grid)
+    want = torch.from_numpy(c32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(c16, want)
+
+
 def test_tiny_workload_end_to_end():
     """256x256 A (2 outlier columns) times W^T: oracle-quantized operands, GPU bytes must match."""
     d = synth.tiny()
