@@ -117,6 +117,17 @@ def quantize_lines(bits, grid=E2M1, rounding=RTNE, seed=0, stream=STREAM_ROW_SR,
         y = rotate_lines(bits, had_n, signs)
     else:
         y = bf16_bits_to_f64(bits).astype(np.float32)
+    return quantize_values(y, grid, rounding, seed, stream, block, line_ids)
+
+
+def quantize_values(y, grid=E2M1, rounding=RTNE, seed=0, stream=STREAM_ROW_SR, block=32, line_ids=None):
+    """Steps 2-5 on float32 values y (lines, length): absmax, scale, cast, pack.
+
+    Same outputs and element indexing as quantize_lines.
+    """
+    y = np.asarray(y, dtype=np.float32)
+    assert y.ndim == 2 and grid in (E2M1, E1M2) and rounding in (RTNE, SR) and block in BLOCK_SIZES
+    lines, length = y.shape
 
     # pad to whole blocks (oracle-only tails: zeros do not change the absmax)
     nblk = -(-length // block)
