@@ -6,4 +6,4 @@ of include/mxfp4.h).  This package holds its ctypes binding, torch-facing
 wrappers (torch supplies device memory and streams only), the training-step
 orchestration of the three GEMMs, and the seeded synthetic inputs.
 """
-from .api import QTensor, quantize, gemm, empty_qtensor  # noqa: F401
+from .api import QTensor, quantize, gemm, empty_qtensor, mxnorm_quantize, mxnorm_correction  # noqa: F401

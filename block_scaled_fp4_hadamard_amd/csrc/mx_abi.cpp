@@ -145,6 +145,37 @@ mx_status mx_gemm(const mx_qtensor* a, const mx_qtensor* b, int64_t M, int64_t N
   return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
 }
 
+mx_status mx_mxnorm_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t power, float c,
+                             mx_grid grid, mx_round round, uint64_t seed, const mx_qtensor* out, float* rho,
+                             void* hip_stream) {
+  if (rows < 0 || cols < 0) return MX_ERR_INVALID;
+  if (power != 1 && power != 2) return MX_ERR_INVALID;
+  if (!(c > 0.0f) || c > 3.0e38f) return MX_ERR_INVALID;          // rejects NaN, non-positive and infinite c
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (round != MX_ROUND_RTNE && round != MX_ROUND_SR) return MX_ERR_INVALID;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (cols % 32 != 0 || cols > 65536) return MX_ERR_INVALID;
+  if (x == nullptr || !aligned16(x)) return MX_ERR_INVALID;
+  if (ld_x < cols || ld_x % 8 != 0) return MX_ERR_INVALID;
+  mx_status s = check_qtensor(out, rows, cols, 32);
+  if (s != MX_OK) return s;
+  if (rho == nullptr || ((uintptr_t)rho & 3u) != 0) return MX_ERR_INVALID;
+  mx::MxNormParams p{};
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld_x = ld_x;
+  p.codes = out->codes;
+  p.ld_codes = out->ld_codes;
+  p.scales = out->scales;
+  p.ld_scales = out->ld_scales;
+  p.rho = rho;
+  p.c = c;
+  p.seed = seed;
+  hipError_t e = mx::launch_mxnorm(p, power, grid, round, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
 const char* mx_status_str(mx_status status) {
   switch (status) {
     case MX_OK: return "MX_OK";

@@ -1,12 +1,63 @@
-// Device-side helpers shared by the quantizer kernels: Philox4x32-10, the
-// exact fallback for the Hadamard sums, and small bit utilities.
+// Device-side helpers shared by the quantizer kernels: the MX cast of one
+// value, Philox4x32-10, the exact fallback for the Hadamard sums, and small
+// bit utilities.
 // gfx950 (CDNA4) only.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "../../include/mxfp4.h"
 
 namespace mx {
 
+// ---------------------------------------------------------------------------
+// The MX cast of one value: E8M0 scale as a float, 4-bit code, scale byte.
+
+__device__ __forceinline__ uint32_t e8m0_scale_bits(uint32_t byte) {
+  // the float whose exponent the scaled conversions divide by: 2^(byte-127)
+  return byte ? (byte << 23) : 0x00400000u;        // 2^-127 is a subnormal float
+}
+
+// 4-bit code of one value y of a block with scale byte `byte` (finite y):
+// sign bit 3, magnitude code = |y| / 2^(byte-127) on the grid, rounded by
+// RTNE, or (SR) up from the level below iff floor(frac * 2^22) + (u >> 10)
+// >= 2^22 for the element's random word u; saturating at the top level.
+template <int GRID, int ROUND>
+__device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const float sc = __uint_as_float(e8m0_scale_bits(byte));
+  if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yy, 0.0f, sc, 0) & 0xFu;
+  } else if constexpr (GRID == MX_GRID_E2M1) {
+    // gfx950's stochastic fp4 conversion applies exactly this rule (the
+    // element's own word; the pair's second value is a placeholder, and the
+    // other result bytes are not kept)
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (v2f){yy, 0.0f}, u, sc, 0) & 0xFu;
+  } else {
+    // uniform grid: magnitude code = |y| * 2^(2-e), rounded
+    const int ebias = (int)byte - 127;
+    const float t = ldexpf(fabsf(yy), 2 - ebias);
+    uint32_t k;
+    if constexpr (ROUND == MX_ROUND_RTNE) {
+      k = (uint32_t)rintf(t);
+    } else {
+      const float fl = floorf(t);
+      const uint32_t p22 = (uint32_t)ldexpf(t - fl, 22);     // floor(frac * 2^22); t - fl is exact
+      k = (uint32_t)fl + ((p22 + (u >> 10)) >> 22);
+    }
+    return min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
+  }
+}
+
+// Scale byte of a block whose largest |y| has float exponent field expf.
+template <int GRID>
+__device__ __forceinline__ uint32_t scale_byte(uint32_t expf) {
+  constexpr uint32_t kEmax = GRID == MX_GRID_E2M1 ? 2u : 0u;
+  return expf > kEmax ? expf - kEmax : 0u;
+}
+
+// Cast one 32-element block y[] of finite values into 4 code dwords; returns
+// the scale byte.  For SR, y[i] draws Philox word i % 4 of counter block
+// ctr + i / 4 (stream `stream`, key k0:k1).
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies on a 128-bit counter, Weyl-bumped 64-bit key.  The key

@@ -38,4 +38,18 @@ struct GemmParams {
 
 hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s);
 
+struct MxNormParams {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  uint8_t* codes;
+  int64_t ld_codes;
+  uint8_t* scales;
+  int64_t ld_scales;
+  float* rho;
+  float c;
+  uint64_t seed;
+};
+
+hipError_t launch_mxnorm(const MxNormParams& p, int power, int grid_kind, int round, hipStream_t s);
+
 }  // namespace mx

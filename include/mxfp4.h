@@ -13,6 +13,9 @@
  *    scale per block derived from the block's absolute maximum.
  *  - "Résumé Technique : TetraJet-v2", section 2.A: stochastic rounding with
  *    E[round(x)] = x.
+ *  - "MXNorm: Reusing MXFP block scales ...", Sommario tecnico 2: row
+ *    normalization by an inverse-RMS estimate built from the block maxima,
+ *    fused with the cast (mx_mxnorm_quantize).
  *
  * Data layout (all row-major, strides in the units named):
  *  - Input x: bf16 bit patterns, x[r * ld_x + c], 0 <= r < rows, 0 <= c < cols.
@@ -29,8 +32,9 @@
  * The cast: e = clamp(floor(log2 amax) - emax, -127, 127) per block of 32
  * (emax 2 for E2M1, 0 for E1M2; amax 0 gives -127); v = |y| / 2^e goes to the
  * grid by round-to-nearest-even (ties to the even code, saturating at the top
- * level) or by stochastic rounding: with lo <= v < hi adjacent levels,
- * P = floor((v - lo) / (hi - lo) * 2^32), round up iff u < P, where u is word
+ * level) or by stochastic rounding: with lo <= v < hi adjacent levels and
+ * f = (v - lo) / (hi - lo), round up iff floor(f * 2^22) + (u >> 10) >= 2^22
+ * (add-and-truncate on the top 22 bits of u), where u is word
  * (i mod 4) of Philox4x32-10(key = seed, counter = (i div 4, stream, 0)) for
  * the element at index i of the output's logical row-major order (row-wise:
  * r*cols + c, stream 0; column-wise: c*rows + r, stream 1).  A block holding a
@@ -134,6 +138,38 @@ mx_status mx_hadamard_quantize(const uint16_t *x, int64_t rows, int64_t cols, in
 mx_status mx_gemm(const mx_qtensor *a, const mx_qtensor *b, int64_t M, int64_t N, int64_t K,
                   mx_grid grid, int32_t block, void *c, int64_t ldc, mx_out out,
                   void *hip_stream);
+
+/*
+ * mx_mxnorm_quantize: MXNorm fused with the row-wise MX cast ("MXNorm: Reusing
+ * MXFP block scales for efficient tensor normalisation", Sommario tecnico 2).
+ * Row t is scaled by rho_t = c * ((1/K) sum_k m_tk^p)^(-1/p), the inverse-RMS
+ * estimate from its K = cols/32 block maxima, and the scaled row is quantized
+ * row-wise (block 32) as by mx_quantize with axis MX_AXIS_ROW.  The gain of
+ * the normalization is not applied (it belongs in the next layer's weights).
+ * Exactly:
+ *   m_tk  = max |x| over block k of row t (bf16 values; NaN counts as +inf);
+ *   S_t   = sum of m_tk^p in float64 as a balanced binary tree over the
+ *           blocks in order (neighbours first), missing blocks of a
+ *           power-of-two count being zeros;
+ *   q_t   = RN64(S_t / K);
+ *   rho_t = RN32 of the exact real number c * q_t^(-1/p) (ties to even;
+ *           +inf on overflow), or 0 when q_t is 0 or +inf;
+ *   y     = RN32(x * rho_t), cast with stochastic-rounding stream 0.
+ *   x          device, 16-byte aligned, bf16 bit patterns
+ *   rows, cols >= 0 (either 0: nothing to do, MX_OK); cols % 32 == 0,
+ *              cols <= 65536
+ *   ld_x       elements between rows; >= cols, multiple of 8
+ *   power      p: 1 or 2 (the pages favour 2)
+ *   c          the correction constant c(p, 32) > 0, finite (for rows of
+ *              i.i.d. normal values E[M^p]^(1/p), M the largest |value| of
+ *              32: about 2.3471 for p = 1 and 2.3895 for p = 2)
+ *   grid, round, seed   as mx_quantize
+ *   out        rows lines of length cols (codes 16-byte aligned)
+ *   rho        device, float[rows], 4-byte aligned: rho_t for the backward pass
+ */
+mx_status mx_mxnorm_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
+                             int32_t power, float c, mx_grid grid, mx_round round, uint64_t seed,
+                             const mx_qtensor *out, float *rho, void *hip_stream);
 
 /* A static, human-readable name for a status code. */
 const char *mx_status_str(mx_status status);

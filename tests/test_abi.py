@@ -91,3 +91,21 @@ def gemm(M=64, N=64, K=128, grid=0, block=32, c=FAKE, ldc=64, out=0, a="d", b="d
 ])
 def test_gemm_validation(kw, want):
     assert gemm(**kw) == want
+
+
+def mxnorm(x=FAKE, rows=8, cols=128, ld=128, power=2, c=2.39, grid=0, rnd=0, out="d", rho=FAKE):
+    out = q() if out == "d" else out
+    return _lib.mx_mxnorm_quantize(x, rows, cols, ld, power, c, grid, rnd, 0, out, rho, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), 1), (dict(power=3), 1), (dict(power=0), 1), (dict(c=0.0), 1), (dict(c=-1.0), 1),
+    (dict(c=float("nan")), 1), (dict(c=float("inf")), 1), (dict(grid=5), 1), (dict(rnd=2), 1),
+    (dict(cols=120, ld=128), 1),                                # cols % 32
+    (dict(cols=65568, ld=65568, out=q(ld_codes=32784, ld_scales=2049)), 1),   # cols <= 65536
+    (dict(x=0), 1), (dict(x=FAKE + 8), 1), (dict(ld=100), 1), (dict(ld=132), 1),
+    (dict(out=q(ld_codes=32)), 1), (dict(out=q(codes=FAKE + 4)), 1), (dict(rho=0), 1), (dict(rho=FAKE + 2), 1),
+    (dict(rows=0), 0), (dict(cols=0), 0),                       # empty: nothing to do
+])
+def test_mxnorm_validation(kw, want):
+    assert mxnorm(**kw) == want
