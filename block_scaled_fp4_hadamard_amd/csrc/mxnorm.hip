@@ -16,14 +16,17 @@
 //   y     RN32(x * rho), then the cast of the row-wise quantizer (block
 //         absmax, E8M0 scale, RTNE or stochastic rounding on stream 0, pack).
 //
-// One wave per row.  The row is read in chunks of 512 values (16 bytes per
-// lane, 16 blocks per chunk, four lanes per block).  A chunk's 16 block
-// values meet in a butterfly across lanes 4, 8, 16 and 32 apart, which is the
-// balanced tree over those 16 blocks; the chunk sums go to LDS and a second
-// butterfly over up to 128 chunk slots finishes the tree.  rho starts from a
-// float64 estimate and is corrected to the exactly rounded value with
-// midpoint tests whose sign an FMA gives exactly.  Rows of up to 4096 values
-// stay in registers for the second pass; longer rows are read again.
+// One wave per row.  The row is read in groups of 8 chunks of 512 values
+// (16 bytes per lane per chunk, 16 blocks per chunk, four lanes per block),
+// all 8 loads of a group in flight together.  A chunk's 16 block values meet
+// in a butterfly across lanes 4, 8, 16 and 32 apart, which is the balanced
+// tree over those 16 blocks; the 8 chunk sums add as a tree in registers, and
+// the sums of up to 16 groups in a butterfly through LDS: one balanced tree
+// over 2048 block slots, the empty ones zero.  rho starts from a float64
+// estimate and is corrected to the exactly rounded value with midpoint tests
+// whose sign an FMA gives exactly.  The first group (rows up to 4096 values:
+// the whole row) stays in registers for the second pass; later groups are
+// read again.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "mx_device.h"
@@ -33,8 +36,8 @@ namespace mx {
 
 constexpr int kNormWaves = 4;                 // rows per 256-lane workgroup
 constexpr int kChunk = 512;                   // values per chunk: 64 lanes x 8
-constexpr int kMaxChunks = 128;               // cols <= 65536
-constexpr int kRegChunks = 8;                 // rows up to 4096 values stay in registers
+constexpr int kGroupChunks = 8;               // chunks loaded together (4096 values)
+constexpr int kMaxGroups = 16;                // cols <= 65536
 
 // |x| of 8 bf16 values as magnitude bits; the largest, with NaN above +inf
 __device__ __forceinline__ uint32_t max_mag8(const uint4& v) {
@@ -90,105 +93,134 @@ __device__ float estimate_rho(double q, float c) {
   return f;
 }
 
-template <int GRID, int ROUND, int P, bool REGS>
+// chunk ch (0 .. 7) of group g of a row: 8 bf16 per lane, zeros past the row's end
+__device__ __forceinline__ void load_group(const uint16_t* xr, int64_t cols, int g, int lane, uint4 (&v)[kGroupChunks]) {
+#pragma unroll
+  for (int ch = 0; ch < kGroupChunks; ++ch) {
+    const int64_t col = ((int64_t)g * kGroupChunks + ch) * kChunk + 8 * lane;
+    v[ch] = col < cols ? *(const uint4*)(xr + col) : uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+// tree sum of m^p over the 128 blocks of a group: within each chunk by a lane
+// butterfly (quads 1, 2, 4, 8 apart), then over the 8 chunks in registers
+template <int P>
+__device__ __forceinline__ double group_sum(const uint4 (&v)[kGroupChunks]) {
+  double s[kGroupChunks];
+#pragma unroll
+  for (int ch = 0; ch < kGroupChunks; ++ch) {
+    uint32_t mb = quad_max(max_mag8(v[ch]));
+    if (mb > 0x7F80u) mb = 0x7F80u;                           // NaN counts as +inf
+    const double m = (double)__uint_as_float(mb << 16);
+    s[ch] = P == 1 ? m : m * m;                               // exact
+  }
+#pragma unroll
+  for (int d = 4; d <= 32; d <<= 1)
+#pragma unroll
+    for (int ch = 0; ch < kGroupChunks; ++ch) s[ch] += __shfl_xor(s[ch], d);
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
+// cast 8 values of one lane (a quarter of block col / 32) into a code word;
+// returns the block's scale byte
+template <int GRID, int ROUND>
+__device__ __forceinline__ uint32_t cast8(const uint4& v, float rho, int64_t elem, uint32_t k0, uint32_t k1,
+                                          uint32_t& word) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float y[8];
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[2 * i] = __uint_as_float(w[i] << 16) * rho;
+    y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * rho;
+    mb = max(mb, max(__float_as_uint(y[2 * i]) & 0x7FFFFFFFu, __float_as_uint(y[2 * i + 1]) & 0x7FFFFFFFu));
+  }
+  mb = quad_max(mb);
+  const bool nonfinite = mb >= 0x7F800000u;
+  const uint32_t byte = nonfinite ? 0xFFu : scale_byte<GRID>(mb >> 23);
+  uint32_t r = 0;
+  if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
+    const float sc = __uint_as_float(e8m0_scale_bits(byte));
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[0], y[1], sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], sc, 3);
+  } else {
+    uint32_t u[8] = {};
+    if constexpr (ROUND == MX_ROUND_SR) {
+      const uint64_t i0 = (uint64_t)elem >> 2;                // element index / 4 (elem % 8 == 0)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const U4 q = philox4x32_10((uint32_t)(i0 + h), (uint32_t)((i0 + h) >> 32), 0u, 0u, k0, k1);
+        u[4 * h] = q.x;
+        u[4 * h + 1] = q.y;
+        u[4 * h + 2] = q.z;
+        u[4 * h + 3] = q.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r |= cast_one<GRID, ROUND>(y[i], byte, u[i]) << (4 * i);
+  }
+  word = nonfinite ? 0u : r;
+  return byte;
+}
+
+template <int GRID, int ROUND, int P>
 __global__ void __launch_bounds__(64 * kNormWaves) mxnorm_kernel(const MxNormParams p) {
-  __shared__ double chunk_sums[kNormWaves][kMaxChunks];
+  __shared__ double group_sums[kNormWaves][kMaxGroups];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kNormWaves + wave;
   if (row >= p.rows) return;                                   // the whole wave
-  const int nch = (int)((p.cols + kChunk - 1) / kChunk);
+  const int ngroups = (int)((p.cols + kGroupChunks * kChunk - 1) / (kGroupChunks * kChunk));
   const uint16_t* xr = p.x + row * p.ld_x;
-  double* sums = chunk_sums[wave];
 
-  // ---- pass 1: block maxima, m^p, the tree sum
-  uint4 keep[REGS ? kRegChunks : 1];
-#pragma unroll
-  for (int i = 0; i < (REGS ? kRegChunks : 1); ++i) keep[i] = uint4{0u, 0u, 0u, 0u};
-  for (int ch = 0; ch < nch; ++ch) {
-    const int64_t col = (int64_t)ch * kChunk + 8 * lane;
-    uint4 v = uint4{0u, 0u, 0u, 0u};
-    if (col < p.cols) v = *(const uint4*)(xr + col);
-    if constexpr (REGS) {
-#pragma unroll
-      for (int i = 0; i < kRegChunks; ++i)
-        if (i == ch) keep[i] = v;
+  // ---- pass 1: block maxima, m^p, the tree sum (groups of 8 chunks; the
+  // group sums meet in a 16-slot butterfly)
+  uint4 v[kGroupChunks];
+  load_group(xr, p.cols, 0, lane, v);
+  double total = group_sum<P>(v);
+  if (ngroups > 1) {
+    if (lane == 0) group_sums[wave][0] = total;
+    for (int g = 1; g < ngroups; ++g) {
+      uint4 w[kGroupChunks];
+      load_group(xr, p.cols, g, lane, w);
+      const double gs = group_sum<P>(w);
+      if (lane == 0) group_sums[wave][g] = gs;
     }
-    uint32_t mb = quad_max(max_mag8(v));
-    if (mb > 0x7F80u) mb = 0x7F80u;                           // NaN counts as +inf
-    const double m = (double)__uint_as_float(mb << 16);
-    double s = P == 1 ? m : m * m;                            // exact
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 8);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    if (lane == 0) sums[ch] = s;
+    __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0): the sums are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // a butterfly over all 64 lanes (slots past the groups are zeros), so
+    // that every lane ends with the same total
+    double t = lane < ngroups ? group_sums[wave][lane] : 0.0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) t += __shfl_xor(t, d);
+    total = t;
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt(0): the sums are in LDS
-  __builtin_amdgcn_wave_barrier();
-  double t = (2 * lane < nch ? sums[2 * lane] : 0.0) + (2 * lane + 1 < nch ? sums[2 * lane + 1] : 0.0);
-  t += __shfl_xor(t, 1);
-  t += __shfl_xor(t, 2);
-  t += __shfl_xor(t, 4);
-  t += __shfl_xor(t, 8);
-  t += __shfl_xor(t, 16);
-  t += __shfl_xor(t, 32);
-  const double q = t / (double)(p.cols / 32);
+  const double q = total / (double)(p.cols / 32);
   const float rho = estimate_rho<P>(q, p.c);
   if (lane == 0) p.rho[row] = rho;
 
-  // ---- pass 2: y = RN32(x * rho), block scale, cast, pack
+  // ---- pass 2: y = RN32(x * rho), block scale, cast, pack (the first
+  // group is still in registers)
   const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
-  for (int ch = 0; ch < nch; ++ch) {
-    const int64_t col = (int64_t)ch * kChunk + 8 * lane;
-    uint4 v = uint4{0u, 0u, 0u, 0u};
-    if constexpr (REGS) {
+  for (int g = 0; g < ngroups; ++g) {
+    if (g > 0) load_group(xr, p.cols, g, lane, v);
 #pragma unroll
-      for (int i = 0; i < kRegChunks; ++i)
-        if (i == ch) v = keep[i];
-    } else {
-      if (col < p.cols) v = *(const uint4*)(xr + col);
-    }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float y[8];
-    uint32_t mb = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[2 * i] = __uint_as_float(w[i] << 16) * rho;
-      y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * rho;
-      mb = max(mb, max(__float_as_uint(y[2 * i]) & 0x7FFFFFFFu, __float_as_uint(y[2 * i + 1]) & 0x7FFFFFFFu));
-    }
-    mb = quad_max(mb);
-    const bool nonfinite = mb >= 0x7F800000u;
-    const uint32_t byte = nonfinite ? 0xFFu : scale_byte<GRID>(mb >> 23);
-    uint32_t u[8] = {};
-    if constexpr (ROUND == MX_ROUND_SR) {
-      const uint64_t i0 = ((uint64_t)row * (uint64_t)p.cols + (uint64_t)col) >> 2;   // element index / 4
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const U4 r = philox4x32_10((uint32_t)(i0 + h), (uint32_t)((i0 + h) >> 32), 0u, 0u, k0, k1);
-        u[4 * h] = r.x;
-        u[4 * h + 1] = r.y;
-        u[4 * h + 2] = r.z;
-        u[4 * h + 3] = r.w;
+    for (int ch = 0; ch < kGroupChunks; ++ch) {
+      const int64_t col = ((int64_t)g * kGroupChunks + ch) * kChunk + 8 * lane;
+      uint32_t word;
+      const uint32_t byte = cast8<GRID, ROUND>(v[ch], rho, row * p.cols + col, k0, k1, word);
+      if (col < p.cols) {
+        *(uint32_t*)(p.codes + row * p.ld_codes + col / 2) = word;
+        if ((lane & 3) == 0) p.scales[row * p.ld_scales + col / 32] = (uint8_t)byte;
       }
-    }
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) word |= cast_one<GRID, ROUND>(y[i], byte, u[i]) << (4 * i);
-    if (nonfinite) word = 0;
-    if (col < p.cols) {
-      *(uint32_t*)(p.codes + row * p.ld_codes + col / 2) = word;
-      if ((lane & 3) == 0) p.scales[row * p.ld_scales + col / 32] = (uint8_t)byte;
     }
   }
 }
 
 template <int GRID, int ROUND, int P>
 static void launch_p(const MxNormParams& p, dim3 g, hipStream_t s) {
-  if (p.cols <= (int64_t)kRegChunks * kChunk)
-    hipLaunchKernelGGL((mxnorm_kernel<GRID, ROUND, P, true>), g, dim3(64 * kNormWaves), 0, s, p);
-  else
-    hipLaunchKernelGGL((mxnorm_kernel<GRID, ROUND, P, false>), g, dim3(64 * kNormWaves), 0, s, p);
+  hipLaunchKernelGGL((mxnorm_kernel<GRID, ROUND, P>), g, dim3(64 * kNormWaves), 0, s, p);
 }
 
 template <int GRID, int ROUND>
