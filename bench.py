@@ -15,8 +15,9 @@ before timing starts.
 
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
-with each family's achieved HBM GB/s or MFMA TFLOP/s; `roofline` is the
-dominant kernel's; `cpu_baseline` is the CPU oracle on a bounded sample.
+with each family's achieved HBM GB/s or MFMA TFLOP/s; `mxnorm` times the fused
+MXNorm + row-wise cast launch apart from the step; `roofline` is the dominant
+kernel's; `cpu_baseline` is the CPU oracle on a bounded sample.
 """
 import argparse
 import json
@@ -103,6 +104,38 @@ def cpu_baseline(tokens=512):
                       "+ Fprop/Dgrad/Wgrad fp64 GEMMs; %.1f s" % (tokens, dt)}
 
 
+def measure_mxnorm(tensors, dev, reps=30):
+    """The MXNorm + row-wise MX cast launch on the block's 4096-wide tensors, timed apart from the step.
+
+    Six 8192 x 4096 bf16 tensors (403 MB, more than the last-level cache) in rotation, p = 2 with the Monte
+    Carlo constant, E2M1 RTNE; algorithmic bytes per launch: the bf16 read, codes and scales, rho.
+    """
+    import torch
+    from block_scaled_fp4_hadamard_amd import mxnorm_quantize
+    names = ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"]
+    xs = [tensors[n] for n in names]
+    rows, cols = xs[0].shape
+    outs = [mxnorm_quantize(x, power=2) for x in xs]
+    for i, x in enumerate(xs):
+        mxnorm_quantize(x, power=2, out=outs[i][0], rho=outs[i][1])
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for j in range(reps):
+        i = j % len(xs)
+        mxnorm_quantize(xs[i], power=2, out=outs[i][0], rho=outs[i][1])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 32 + rows * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "MXNorm (p=2) fused with the row-wise E2M1 RTNE cast, %dx%d bf16 rows, %d tensors in "
+                        "rotation" % (rows, cols, len(xs)),
+            "us_per_launch": round(us, 2), "bytes_per_launch": nbytes, "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,6 +214,7 @@ def main():
         achieved = f["bytes"] / f["launches"] / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom}
+    mxnorm = measure_mxnorm(tensors, dev)
     qms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("quant"))
     gms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("gemm"))
     quant_gbs = step.quant_bytes / (qms * 1e-3) / 1e9
@@ -209,6 +243,7 @@ def main():
         "gemm": {"TFLOP/s": round(gemm_tf, 1), "frac_mfma": round(gemm_tf / FP4_PEAK_TFLOPS, 4),
                  "ms_per_step": round(gms, 4)},
         "kernels": kernels,
+        "mxnorm": mxnorm,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -8,7 +8,7 @@
         counter scaled by what it reads for a plain device copy of N bytes (N read + N written)
 
 Kernel families: quant.rtne / quant.sr (the quantizer by rounding mode), gemm.bf16 / gemm.f32 (the GEMM by
-output type), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
+output type), mxnorm (the fused MXNorm cast), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
 reader can tell when the figures no longer describe the code.
 """
 import argparse
@@ -21,7 +21,7 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("quant.hip", "gemm.hip", "mx_device.h", "mx_kernels.h")
+KERNEL_SOURCES = ("quant.hip", "gemm.hip", "mxnorm.hip", "mx_device.h", "mx_kernels.h")
 
 
 def sources_hash():
@@ -39,6 +39,8 @@ def kernel_family(name):
     m = re.search(r"gemm_\w*kernel<(\d+), (\d+)>", name)
     if m:
         return "gemm.bf16" if m.group(2) == "1" else "gemm.f32"
+    if "mxnorm_kernel" in name:
+        return "mxnorm"
     if "copyBuffer" in name or "copy" in name.lower():
         return "copy"
     return None
