@@ -16,8 +16,8 @@ AXIS = {"row": 1, "col": 2, "both": 3}
 HAD = {"none": 0, "det": 1, "rand": 2}
 OUT = {"f32": 0, "bf16": 1}
 
-EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_mxnorm_quantize", "mx_status_str",
-           "mx_version")
+EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_mxnorm_quantize", "mx_quant_stats",
+           "mx_status_str", "mx_version")
 
 
 class MXError(RuntimeError):
@@ -51,6 +51,8 @@ def lib():
         L.mx_gemm.restype = ctypes.c_int
         L.mx_mxnorm_quantize.argtypes = [vp, i64, i64, i64, i32, ctypes.c_float, i32, i32, u64, qp, vp, vp]
         L.mx_mxnorm_quantize.restype = ctypes.c_int
+        L.mx_quant_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, qp, vp, vp]
+        L.mx_quant_stats.restype = ctypes.c_int
         L.mx_status_str.argtypes = [ctypes.c_int]
         L.mx_status_str.restype = ctypes.c_char_p
         L.mx_version.argtypes = []
@@ -92,3 +94,8 @@ def mx_gemm(a_q, b_q, M, N, K, grid, block, c_ptr, ldc, out, stream):
 def mx_mxnorm_quantize(x_ptr, rows, cols, ld_x, power, c, grid, rnd, seed, out_q, rho_ptr, stream):
     return lib().mx_mxnorm_quantize(x_ptr, rows, cols, ld_x, power, c, grid, rnd, seed, ctypes.byref(out_q),
                                     rho_ptr, stream)
+
+
+def mx_quant_stats(x_ptr, rows, cols, ld_x, axis, grid, had_n, had_kind, had_seed, q, stats_ptr, stream):
+    return lib().mx_quant_stats(x_ptr, rows, cols, ld_x, axis, grid, had_n, had_kind, had_seed, ctypes.byref(q),
+                                stats_ptr, stream)

@@ -142,3 +142,28 @@ def mxnorm_quantize(x, power=2, c=None, grid="e2m1", rounding="rtne", seed=0, ou
                                  _lib.ROUND[rounding], seed, q.c_struct(), r.data_ptr(), _stream(dev))
     _lib.check(st, "mx_mxnorm_quantize")
     return q, r
+
+
+def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0, stats=None):
+    """Diagnostics of one quantized output q of x: SQNR (dB), noise and signal energy, magnitude-code counts,
+    effective bucket ratio (exp(entropy) / 8).  stats: an optional zeroed float64 (12,) CUDA tensor to reuse.
+    """
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    xb = _bits_view(x)
+    rows, cols = x.shape
+    grid = grid or q.grid
+    buf = stats if stats is not None else torch.zeros(12, dtype=torch.float64, device=x.device)
+    st = _lib.mx_quant_stats(xb.data_ptr(), rows, cols, xb.stride(0), _lib.AXIS[axis], _lib.GRID[grid],
+                             had_n, _lib.HAD["none" if not had_n else had_kind], had_seed, q.c_struct(),
+                             buf.data_ptr(), _stream(x.device))
+    _lib.check(st, "mx_quant_stats")
+    host = buf.cpu()
+    sums = host[:2].numpy()
+    counts = host[2:].view(torch.int64).numpy()
+    hist, blocks = counts[:8].copy(), int(counts[8])
+    p = hist[hist > 0] / max(hist.sum(), 1)
+    ratio = float(np.exp(-np.sum(p * np.log(p))) / 8.0) if p.size else 0.0
+    sqnr = float("inf") if sums[1] == 0 else float(10.0 * np.log10(sums[0] / sums[1]))
+    return {"sqnr_db": sqnr, "sum_sq": float(sums[0]), "sum_err_sq": float(sums[1]), "hist": hist.tolist(),
+            "blocks": blocks, "bucket_ratio": ratio}

@@ -176,6 +176,44 @@ mx_status mx_mxnorm_quantize(const uint16_t* x, int64_t rows, int64_t cols, int6
   return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
 }
 
+mx_status mx_quant_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, mx_axis axis, mx_grid grid,
+                         int32_t had_n, mx_had had_kind, uint64_t had_seed, const mx_qtensor* q,
+                         mx_quant_stats_t* stats, void* hip_stream) {
+  if (rows < 0 || cols < 0) return MX_ERR_INVALID;
+  if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL) return MX_ERR_INVALID;
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (had_kind != MX_HAD_NONE && had_kind != MX_HAD_DET && had_kind != MX_HAD_RAND) return MX_ERR_INVALID;
+  if (had_kind == MX_HAD_NONE) had_n = 0;
+  else if (had_n != 16 && had_n != 32) return MX_ERR_INVALID;
+  if (stats == nullptr || ((uintptr_t)stats & 7u) != 0) return MX_ERR_INVALID;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (x == nullptr || ((uintptr_t)x & 1u) != 0 || ld_x < cols) return MX_ERR_INVALID;
+  const bool col = axis == MX_AXIS_COL;
+  const int64_t lines = col ? cols : rows, len = col ? rows : cols;
+  if (len % 32 != 0) return MX_ERR_INVALID;
+  mx_status s = check_qtensor(q, lines, len, 32);
+  if (s != MX_OK) return s;
+  mx::QuantStatsParams p{};
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld_x = ld_x;
+  p.codes = q->codes;
+  p.ld_codes = q->ld_codes;
+  p.scales = q->scales;
+  p.ld_scales = q->ld_scales;
+  p.axis_col = col ? 1 : 0;
+  p.grid = grid;
+  p.sign_mask = 0u;
+  if (had_kind == MX_HAD_RAND) {
+    const uint32_t w0 = philox_word0(0u, 0u, 2u, 0u, (uint32_t)had_seed, (uint32_t)(had_seed >> 32));
+    p.sign_mask = had_n == 32 ? w0 : (w0 & 0xFFFFu);
+  }
+  p.out = stats;
+  hipError_t e = mx::launch_quant_stats(p, had_n, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
 const char* mx_status_str(mx_status status) {
   switch (status) {
     case MX_OK: return "MX_OK";

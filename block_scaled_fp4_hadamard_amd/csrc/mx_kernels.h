@@ -52,4 +52,19 @@ struct MxNormParams {
 
 hipError_t launch_mxnorm(const MxNormParams& p, int power, int grid_kind, int round, hipStream_t s);
 
+struct QuantStatsParams {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  const uint8_t* codes;
+  int64_t ld_codes;
+  const uint8_t* scales;
+  int64_t ld_scales;
+  int axis_col;         // 0: row-wise output (blocks along rows), 1: column-wise
+  int grid;
+  uint32_t sign_mask;   // bit j set: input j of every Hadamard chunk is negated
+  mx_quant_stats_t* out;
+};
+
+hipError_t launch_quant_stats(const QuantStatsParams& p, int had_n, hipStream_t s);
+
 }  // namespace mx

@@ -81,6 +81,14 @@ typedef enum { MX_AXIS_ROW = 1, MX_AXIS_COL = 2, MX_AXIS_BOTH = 3 } mx_axis;   /
 typedef enum { MX_HAD_NONE = 0, MX_HAD_DET = 1, MX_HAD_RAND = 2 } mx_had;
 typedef enum { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out;
 
+/* Totals of mx_quant_stats (see there); 8-byte aligned device memory. */
+typedef struct {
+  double sum_sq;       /* sum of y^2 over the counted blocks */
+  double sum_err_sq;   /* sum of (y - y_hat)^2 */
+  uint64_t hist[8];    /* count of every magnitude code 0..7 */
+  uint64_t blocks;     /* 32-value blocks counted */
+} mx_quant_stats_t;
+
 typedef struct {
   uint8_t *codes;     /* device: [lines][K/2] packed 4-bit codes */
   int64_t ld_codes;   /* bytes between lines; >= K/2, multiple of 16 */
@@ -170,6 +178,32 @@ mx_status mx_gemm(const mx_qtensor *a, const mx_qtensor *b, int64_t M, int64_t N
 mx_status mx_mxnorm_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
                              int32_t power, float c, mx_grid grid, mx_round round, uint64_t seed,
                              const mx_qtensor *out, float *rho, void *hip_stream);
+
+/*
+ * mx_quant_stats: diagnostics of a quantized tensor ("Ripensare il Bias di
+ * Shrinkage nel Pretraining di LLM in FP4", Risultati Sperimentali,
+ * Diagnostica di Quantizzazione: SQNR and bucket usage with and without the
+ * rotation, E2M1 against E1M2).  Adds to *stats, over every block whose scale
+ * byte is not 0xFF: sum of y^2, sum of (y - y_hat)^2, the counts of the 8
+ * magnitude codes and the number of blocks.  y are the values the cast
+ * received (x, or its rotation as defined for mx_hadamard_quantize, formed
+ * with float64 butterflies: exact for chunks spanning at most 40 binades,
+ * within float64 rounding otherwise); y_hat is the decoded code times
+ * 2^(scale byte - 127).  SQNR = 10 log10(sum_sq / sum_err_sq).
+ *   x, rows, cols, ld_x   the tensor that was quantized (ld_x >= cols)
+ *   axis       MX_AXIS_ROW or MX_AXIS_COL: which output q is
+ *   grid, had_n, had_kind, had_seed   as passed to the quantizer (had_kind
+ *              MX_HAD_NONE: no rotation)
+ *   q          the quantized output (lines and length as for that axis;
+ *              the quantized axis a multiple of 32)
+ *   stats      device, 8-byte aligned; the caller zeroes it before the first
+ *              call; several calls may accumulate into one total.  The
+ *              float64 sums are added with atomics, so their last bits may
+ *              vary from run to run; the counts are exact.
+ */
+mx_status mx_quant_stats(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, mx_axis axis,
+                         mx_grid grid, int32_t had_n, mx_had had_kind, uint64_t had_seed,
+                         const mx_qtensor *q, mx_quant_stats_t *stats, void *hip_stream);
 
 /* A static, human-readable name for a status code. */
 const char *mx_status_str(mx_status status);

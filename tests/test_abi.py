@@ -109,3 +109,18 @@ def mxnorm(x=FAKE, rows=8, cols=128, ld=128, power=2, c=2.39, grid=0, rnd=0, out
 ])
 def test_mxnorm_validation(kw, want):
     assert mxnorm(**kw) == want
+
+
+def stats_call(x=FAKE, rows=64, cols=128, ld=128, axis=1, grid=0, had_n=0, kind=0, q_="d", st=FAKE):
+    qq = q() if q_ == "d" else q_
+    return _lib.mx_quant_stats(x, rows, cols, ld, axis, grid, had_n, kind, 0, qq, st, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), 1), (dict(axis=3), 1), (dict(axis=0), 1), (dict(grid=4), 1), (dict(kind=7), 1),
+    (dict(had_n=8, kind=1), 1), (dict(st=0), 1), (dict(st=FAKE + 4), 1), (dict(x=0), 1), (dict(x=FAKE + 1), 1),
+    (dict(ld=100), 1), (dict(cols=120, ld=128), 1), (dict(rows=40, axis=2, q_=q(ld_codes=16, ld_scales=1)), 1),
+    (dict(q_=q(ld_codes=32)), 1), (dict(rows=0), 0), (dict(cols=0), 0),
+])
+def test_quant_stats_validation(kw, want):
+    assert stats_call(**kw) == want
