@@ -17,13 +17,19 @@ HAD = {"none": 0, "det": 1, "rand": 2}
 OUT = {"f32": 0, "bf16": 1}
 
 EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_mxnorm_quantize", "mx_quant_stats",
-           "mx_status_str", "mx_version")
+           "mx_nvfp4_quantize", "mx_status_str", "mx_version")
 
 
 class MXError(RuntimeError):
     def __init__(self, status, fn):
         self.status = status
         super().__init__("%s returned %s" % (fn, status_str(status)))
+
+
+class NVTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("inner", ctypes.c_void_p), ("ld_inner", ctypes.c_int64),
+                ("outer", ctypes.c_void_p), ("ld_outer", ctypes.c_int64)]
 
 
 class QTensorC(ctypes.Structure):
@@ -53,6 +59,9 @@ def lib():
         L.mx_mxnorm_quantize.restype = ctypes.c_int
         L.mx_quant_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, qp, vp, vp]
         L.mx_quant_stats.restype = ctypes.c_int
+        np_ = ctypes.POINTER(NVTensorC)
+        L.mx_nvfp4_quantize.argtypes = [vp, i64, i64, i64, i32, i32, u64, np_, np_, vp]
+        L.mx_nvfp4_quantize.restype = ctypes.c_int
         L.mx_status_str.argtypes = [ctypes.c_int]
         L.mx_status_str.restype = ctypes.c_char_p
         L.mx_version.argtypes = []
@@ -99,3 +108,13 @@ def mx_mxnorm_quantize(x_ptr, rows, cols, ld_x, power, c, grid, rnd, seed, out_q
 def mx_quant_stats(x_ptr, rows, cols, ld_x, axis, grid, had_n, had_kind, had_seed, q, stats_ptr, stream):
     return lib().mx_quant_stats(x_ptr, rows, cols, ld_x, axis, grid, had_n, had_kind, had_seed, ctypes.byref(q),
                                 stats_ptr, stream)
+
+
+def nvtensor(codes_ptr, ld_codes, inner_ptr, ld_inner, outer_ptr, ld_outer):
+    return NVTensorC(codes_ptr, ld_codes, inner_ptr, ld_inner, outer_ptr, ld_outer)
+
+
+def mx_nvfp4_quantize(x_ptr, rows, cols, ld_x, rnd, axis, seed, row_q, col_q, stream):
+    return lib().mx_nvfp4_quantize(x_ptr, rows, cols, ld_x, rnd, axis, seed,
+                                   ctypes.byref(row_q) if row_q is not None else None,
+                                   ctypes.byref(col_q) if col_q is not None else None, stream)

@@ -167,3 +167,43 @@ def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0
     sqnr = float("inf") if sums[1] == 0 else float(10.0 * np.log10(sums[0] / sums[1]))
     return {"sqnr_db": sqnr, "sum_sq": float(sums[0]), "sum_err_sq": float(sums[1]), "hist": hist.tolist(),
             "blocks": blocks, "bucket_ratio": ratio}
+
+
+@dataclass
+class NVTensor:
+    """An NVFP4-style double-block operand: L lines of length K.
+
+    codes uint8 (L, K/2) E2M1 as QTensor; inner uint8 (L, K/16) E4M3 scales; outer float32 (L, K/128)
+    """
+    codes: torch.Tensor
+    inner: torch.Tensor
+    outer: torch.Tensor
+
+    def c_struct(self):
+        return _lib.nvtensor(self.codes.data_ptr(), self.codes.stride(0), self.inner.data_ptr(),
+                             self.inner.stride(0), self.outer.data_ptr(), self.outer.stride(0))
+
+
+def nvfp4_quantize(x, axis="row", rounding="rtne", seed=0):
+    """NVFP4-style double-block quantization of a 2-D bf16 CUDA tensor; {"row": NVTensor, "col": NVTensor}."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    xb = _bits_view(x)
+    rows, cols = x.shape
+    dev = x.device
+
+    def empty(lines, k):
+        return NVTensor(torch.empty((lines, k // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((lines, k // 16), dtype=torch.uint8, device=dev),
+                        torch.empty((lines, k // 128), dtype=torch.float32, device=dev))
+    out = {}
+    if axis in ("row", "both"):
+        out["row"] = empty(rows, cols)
+    if axis in ("col", "both"):
+        out["col"] = empty(cols, rows)
+    rq = out["row"].c_struct() if "row" in out else None
+    cq = out["col"].c_struct() if "col" in out else None
+    st = _lib.mx_nvfp4_quantize(xb.data_ptr(), rows, cols, xb.stride(0), _lib.ROUND[rounding], _lib.AXIS[axis],
+                                seed, rq, cq, _stream(dev))
+    _lib.check(st, "mx_nvfp4_quantize")
+    return out

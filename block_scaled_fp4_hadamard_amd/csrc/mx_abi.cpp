@@ -31,7 +31,9 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 mx_status check_qtensor(const mx_qtensor* q, int64_t lines, int64_t k, int32_t block) {
   if (q == nullptr || q->codes == nullptr || q->scales == nullptr) return MX_ERR_INVALID;
-  if (!aligned16(q->codes) || q->ld_codes % 16 != 0) return MX_ERR_INVALID;
+  // the 32-value kernels store 16 code bytes at a time, the 16-value kernel 8
+  const int64_t step = block == 16 ? 8 : 16;
+  if (((uintptr_t)q->codes % (uintptr_t)step) != 0 || q->ld_codes % step != 0) return MX_ERR_INVALID;
   if (q->ld_codes < k / 2 || q->ld_scales < k / block) return MX_ERR_INVALID;
   if (lines > 1 && (q->ld_codes <= 0 || q->ld_scales <= 0)) return MX_ERR_INVALID;
   return MX_OK;
@@ -62,6 +64,27 @@ mx_status quantize_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
     if (rows % block != 0) return MX_ERR_INVALID;
     mx_status s = check_qtensor(col_out, cols, rows, block);
     if (s != MX_OK) return s;
+  }
+  if (block == 16) {
+    // 16-value MX blocks: a separate kernel, no rotation
+    if (had_n != 0) return MX_ERR_UNSUPPORTED;
+    for (int a = 0; a < 2; ++a) {
+      const bool col = a == 1;
+      if (col ? !do_col : !do_row) continue;
+      const mx_qtensor* q = col ? col_out : row_out;
+      mx::Block16Params b{};
+      b.x = x;
+      b.rows = rows;
+      b.cols = cols;
+      b.ld_x = ld_x;
+      b.codes = q->codes;
+      b.ld_codes = q->ld_codes;
+      b.scales = q->scales;
+      b.ld_scales = q->ld_scales;
+      b.seed = seed;
+      if (mx::launch_block16(b, false, grid, round, col, (hipStream_t)stream) != hipSuccess) return MX_ERR_DEVICE;
+    }
+    return MX_OK;
   }
   if (block != 32) return MX_ERR_UNSUPPORTED;
   mx::QuantParams p{};
@@ -212,6 +235,49 @@ mx_status mx_quant_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
   p.out = stats;
   hipError_t e = mx::launch_quant_stats(p, had_n, (hipStream_t)hip_stream);
   return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
+mx_status mx_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, mx_round round,
+                            mx_axis axis, uint64_t seed, const mx_nvfp4_tensor* row_out,
+                            const mx_nvfp4_tensor* col_out, void* hip_stream) {
+  if (rows < 0 || cols < 0) return MX_ERR_INVALID;
+  if (round != MX_ROUND_RTNE && round != MX_ROUND_SR) return MX_ERR_INVALID;
+  if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL && axis != MX_AXIS_BOTH) return MX_ERR_INVALID;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (x == nullptr || !aligned16(x)) return MX_ERR_INVALID;
+  if (ld_x < cols || ld_x % 8 != 0 || cols % 8 != 0) return MX_ERR_INVALID;
+  const bool do_row = (axis & MX_AXIS_ROW) != 0, do_col = (axis & MX_AXIS_COL) != 0;
+  for (int a = 0; a < 2; ++a) {
+    const bool col = a == 1;
+    if (col ? !do_col : !do_row) continue;
+    const mx_nvfp4_tensor* q = col ? col_out : row_out;
+    const int64_t lines = col ? cols : rows, len = col ? rows : cols;
+    if (len % 128 != 0) return MX_ERR_INVALID;
+    if (q == nullptr || q->codes == nullptr || q->inner == nullptr || q->outer == nullptr) return MX_ERR_INVALID;
+    if (!aligned16(q->codes) || q->ld_codes % 16 != 0 || q->ld_codes < len / 2) return MX_ERR_INVALID;
+    if (q->ld_inner < len / 16 || q->ld_outer < len / 128 || ((uintptr_t)q->outer & 3u) != 0) return MX_ERR_INVALID;
+    if (lines > 1 && (q->ld_inner <= 0 || q->ld_outer <= 0)) return MX_ERR_INVALID;
+  }
+  for (int a = 0; a < 2; ++a) {
+    const bool col = a == 1;
+    if (col ? !do_col : !do_row) continue;
+    const mx_nvfp4_tensor* q = col ? col_out : row_out;
+    mx::Block16Params b{};
+    b.x = x;
+    b.rows = rows;
+    b.cols = cols;
+    b.ld_x = ld_x;
+    b.codes = q->codes;
+    b.ld_codes = q->ld_codes;
+    b.scales = q->inner;
+    b.ld_scales = q->ld_inner;
+    b.outer = q->outer;
+    b.ld_outer = q->ld_outer;
+    b.seed = seed;
+    if (mx::launch_block16(b, true, MX_GRID_E2M1, round, col, (hipStream_t)hip_stream) != hipSuccess)
+      return MX_ERR_DEVICE;
+  }
+  return MX_OK;
 }
 
 const char* mx_status_str(mx_status status) {

@@ -67,4 +67,21 @@ struct QuantStatsParams {
 
 hipError_t launch_quant_stats(const QuantStatsParams& p, int had_n, hipStream_t s);
 
+// 16-value blocks along one axis: MX E8M0 scales, or the double-block layout
+// (E4M3 per 16 values in `scales`, float32 per 128 values in `outer`)
+struct Block16Params {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  uint8_t* codes;
+  int64_t ld_codes;
+  uint8_t* scales;
+  int64_t ld_scales;
+  float* outer;
+  int64_t ld_outer;
+  uint64_t seed;
+};
+
+hipError_t launch_block16(const Block16Params& p, bool double_block, int grid_kind, int round, bool col,
+                          hipStream_t s);
+
 }  // namespace mx

@@ -81,6 +81,16 @@ typedef enum { MX_AXIS_ROW = 1, MX_AXIS_COL = 2, MX_AXIS_BOTH = 3 } mx_axis;   /
 typedef enum { MX_HAD_NONE = 0, MX_HAD_DET = 1, MX_HAD_RAND = 2 } mx_had;
 typedef enum { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out;
 
+/* An NVFP4-style double-block operand (mx_nvfp4_quantize): L lines of length K. */
+typedef struct {
+  uint8_t *codes;     /* device: [L][K/2] packed E2M1 codes, as mx_qtensor */
+  int64_t ld_codes;   /* bytes between lines; >= K/2, multiple of 16 */
+  uint8_t *inner;     /* device: [L][K/16] E4M3 scale bytes */
+  int64_t ld_inner;   /* bytes between lines; >= K/16 */
+  float *outer;       /* device: [L][K/128] float32 scales, 4-byte aligned */
+  int64_t ld_outer;   /* floats between lines; >= K/128 */
+} mx_nvfp4_tensor;
+
 /* Totals of mx_quant_stats (see there); 8-byte aligned device memory. */
 typedef struct {
   double sum_sq;       /* sum of y^2 over the counted blocks */
@@ -90,8 +100,8 @@ typedef struct {
 } mx_quant_stats_t;
 
 typedef struct {
-  uint8_t *codes;     /* device: [lines][K/2] packed 4-bit codes */
-  int64_t ld_codes;   /* bytes between lines; >= K/2, multiple of 16 */
+  uint8_t *codes;     /* device: [lines][K/2] packed 4-bit codes; 16-byte aligned (8 with block 16) */
+  int64_t ld_codes;   /* bytes between lines; >= K/2, multiple of 16 (of 8 with block 16) */
   uint8_t *scales;    /* device: [lines][K/block] E8M0 bytes */
   int64_t ld_scales;  /* bytes between lines; >= K/block */
 } mx_qtensor;
@@ -103,7 +113,9 @@ typedef struct {
  *              cols % block == 0 if the row-wise output is requested,
  *              rows % block == 0 if the column-wise output is requested
  *   ld_x       elements between rows; >= cols, multiple of 8, below 2^25
- *   block      32 (the MX block; 16 returns MX_ERR_UNSUPPORTED)
+ *   block      32 (the MX block) or 16 (16-value MX blocks, E8M0 scales
+ *              [L][K/16]; not with a rotation: mx_hadamard_quantize with
+ *              block 16 returns MX_ERR_UNSUPPORTED)
  *   grid       MX_GRID_E2M1 or MX_GRID_E1M2
  *   round      MX_ROUND_RTNE or MX_ROUND_SR (seed keys the Philox draws)
  *   axis       which outputs to write; row_out / col_out must be non-null for
@@ -204,6 +216,31 @@ mx_status mx_mxnorm_quantize(const uint16_t *x, int64_t rows, int64_t cols, int6
 mx_status mx_quant_stats(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, mx_axis axis,
                          mx_grid grid, int32_t had_n, mx_had had_kind, uint64_t had_seed,
                          const mx_qtensor *q, mx_quant_stats_t *stats, void *hip_stream);
+
+/*
+ * mx_nvfp4_quantize: NVFP4-style double-block quantization ("Résumé
+ * Technique : TetraJet-v2", section 2.A: 16-value groups under an 8-bit scale,
+ * inside 128-value outer blocks scaled as a whole, with no tensor-wide absmax).
+ * Along each requested axis (row-wise: along a row; column-wise: the
+ * transpose's rows, i.e. along the token axis):
+ *   s_o = RN32(amax128 / 2688)                 float32 per 128 values
+ *   s_i = E4M3 nearest to amax16 / (6 * s_o)   (ties to even, saturating at
+ *         448; exact quotient), one byte per 16 values
+ *   y   = RN32(RN64(x * RN64(1 / (s_i * s_o)))), cast to E2M1 at unit scale
+ *         by RTNE or the stochastic rule of mx_quantize (stream 0 row-wise,
+ *         1 column-wise), saturating at 6; decoded value = code * s_i * s_o.
+ * s_i = 0 (a zero or underflowing inner block) leaves only the sign bit; an
+ * outer block holding Inf or NaN gets s_o = NaN, inner 0x7F and codes 0.
+ * gfx950's matrix cores take 32-value E8M0 blocks, so mx_gemm does not take
+ * these operands.
+ *   x, rows, cols, ld_x   as mx_quantize (16-byte aligned, ld_x % 8 == 0,
+ *              cols % 8 == 0); the quantized axis a multiple of 128
+ *   round      MX_ROUND_RTNE or MX_ROUND_SR (seed keys the Philox draws)
+ *   axis       which outputs; row_out / col_out non-null for those
+ */
+mx_status mx_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, mx_round round,
+                            mx_axis axis, uint64_t seed, const mx_nvfp4_tensor *row_out,
+                            const mx_nvfp4_tensor *col_out, void *hip_stream);
 
 /* A static, human-readable name for a status code. */
 const char *mx_status_str(mx_status status);

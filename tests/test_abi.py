@@ -19,7 +19,7 @@ FAKE = 0x10000          # an aligned non-null address; validation never derefere
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -59,7 +59,8 @@ def quant(x=FAKE, rows=32, cols=128, ld=128, block=32, grid=0, rnd=0, axis=1, rq
     (dict(rows=40, axis=2), 1),                                 # column output needs rows % 32
     (dict(rq=None), 1), (dict(rq=q(codes=FAKE + 8)), 1), (dict(rq=q(ld_codes=32)), 1),
     (dict(rq=q(ld_codes=72)), 1), (dict(rq=q(ld_scales=2)), 1), (dict(rq=q(scales=0)), 1),
-    (dict(block=16, rq=q(ld_scales=8)), 2),                     # valid, not implemented
+    (dict(block=16, rq=q(ld_codes=68, ld_scales=8)), 1),       # block 16: ld_codes % 8
+    (dict(block=16, rq=q(codes=FAKE + 4, ld_scales=8)), 1),    # block 16: codes 8-byte aligned
     (dict(rows=0), 0), (dict(cols=0), 0),                       # empty: nothing to do
 ])
 def test_quantize_validation(kw, want):
@@ -68,13 +69,15 @@ def test_quantize_validation(kw, want):
 
 def test_hadamard_validation():
     L = _lib
-    def hq(had_n=32, kind=1, block=32):
-        return L.mx_hadamard_quantize(FAKE, 32, 128, 128, block, 0, 0, 1, 0, had_n, kind, 0, q(), None, None)
+    def hq(had_n=32, kind=1, block=32, rq=None):
+        rq = q() if rq is None else rq
+        return L.mx_hadamard_quantize(FAKE, 32, 128, 128, block, 0, 0, 1, 0, had_n, kind, 0, rq, None, None)
     assert hq(had_n=8) == 1
     assert hq(had_n=64) == 1
     assert hq(kind=0) == 1        # the rotating entry point needs a rotation
     assert hq(kind=5) == 1
     assert hq(had_n=32, block=16) == 1   # the rotation must fit in a block
+    assert hq(had_n=16, block=16, rq=q(ld_scales=8)) == 2   # 16-value blocks: no rotation
 
 
 def gemm(M=64, N=64, K=128, grid=0, block=32, c=FAKE, ldc=64, out=0, a="d", b="d"):
@@ -124,3 +127,22 @@ def stats_call(x=FAKE, rows=64, cols=128, ld=128, axis=1, grid=0, had_n=0, kind=
 ])
 def test_quant_stats_validation(kw, want):
     assert stats_call(**kw) == want
+
+
+def nv(x=FAKE, rows=128, cols=256, ld=256, rnd=0, axis=1, rq="d", cq="d"):
+    rq = _lib.nvtensor(FAKE, 128, FAKE, 16, FAKE, 2) if rq == "d" else rq
+    cq = _lib.nvtensor(FAKE, 64, FAKE, 8, FAKE, 1) if cq == "d" else cq
+    return _lib.mx_nvfp4_quantize(x, rows, cols, ld, rnd, axis, 0, rq, cq, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), 1), (dict(rnd=3), 1), (dict(axis=0), 1), (dict(x=0), 1), (dict(x=FAKE + 8), 1),
+    (dict(ld=200), 1), (dict(cols=192, ld=192), 1),             # the quantized axis a multiple of 128
+    (dict(rows=96, axis=2), 1), (dict(rq=None), 1),
+    (dict(rq=_lib.nvtensor(FAKE + 8, 128, FAKE, 16, FAKE, 2)), 1), (dict(rq=_lib.nvtensor(FAKE, 120, FAKE, 16, FAKE, 2)), 1),
+    (dict(rq=_lib.nvtensor(FAKE, 128, FAKE, 15, FAKE, 2)), 1), (dict(rq=_lib.nvtensor(FAKE, 128, FAKE, 16, FAKE + 2, 2)), 1),
+    (dict(rq=_lib.nvtensor(FAKE, 128, FAKE, 16, FAKE, 1)), 1), (dict(rq=_lib.nvtensor(FAKE, 128, 0, 16, FAKE, 2)), 1),
+    (dict(rows=0), 0), (dict(cols=0), 0),
+])
+def test_nvfp4_validation(kw, want):
+    assert nv(**kw) == want

@@ -1,0 +1,72 @@
+"""GPU parity of the 16-value block quantizers against the oracle, bit-exact.
+
+MX blocks of 16 (mx_quantize with block 16) and the NVFP4-style double-block layout ("Résumé Technique :
+TetraJet-v2", section 2.A).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.quantize import quantize_ref
+from oracle.nvfp4 import nvfp4_quantize_ref
+from block_scaled_fp4_hadamard_amd import quantize, synth
+from block_scaled_fp4_hadamard_amd.api import nvfp4_quantize
+from gpu_helpers import announce, to_gpu_bits, qt_to_np, assert_bytes_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def inputs():
+    rng = np.random.default_rng(91)
+    a = synth.activation(128, 384, rng)
+    g = synth.gradient(256, 256, rng)
+    e = synth.activation(128, 256, rng)
+    x = (e.astype(np.uint32) << 16).view(np.float32)
+    x[3, :128] = 0.0                                   # an all-zero outer block
+    x[5, 16:32] = 0.0                                  # an all-zero inner block
+    x[7, 40:56] *= np.float32(2.0 ** -40)              # an inner block that underflows its E4M3 scale
+    x[9] *= np.float32(2.0 ** 100)
+    e = synth.f32_to_bf16_bits(x)
+    e[11, 200] = 0x7FC0                                # NaN
+    e[12, 3] = 0xFF80                                  # -inf
+    e[13, :] = 0x8000                                  # -0
+    return {"activation": a, "gradient": g, "edges": e}
+
+
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_mx_block16(grid, rounding):
+    for name, bits in inputs().items():
+        announce("mx block16 %s %s %s" % (name, grid, rounding))
+        out = quantize(to_gpu_bits(bits), axis="both", grid=grid, rounding=rounding, seed=4, block=16)
+        torch.cuda.synchronize()
+        ref = quantize_ref(bits, "both", grid=grid, rounding=rounding, seed=4, block=16)
+        for key in ("row", "col"):
+            c, s = qt_to_np(out[key])
+            assert_bytes_equal(s, ref[key][1], "%s %s scales" % (name, key))
+            assert_bytes_equal(c, ref[key][0], "%s %s codes" % (name, key))
+
+
+def test_mx_block16_ragged_tail():
+    # 208 values per row: the last 128-value group holds 5 blocks of 16
+    bits = synth.activation(48, 208, np.random.default_rng(92))
+    out = quantize(to_gpu_bits(bits), axis="row", block=16, rounding="sr", seed=2)["row"]
+    torch.cuda.synchronize()
+    ref = quantize_ref(bits, "row", block=16, rounding="sr", seed=2)["row"]
+    c, s = qt_to_np(out)
+    assert_bytes_equal(s, ref[1], "scales")
+    assert_bytes_equal(c, ref[0], "codes")
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_nvfp4_double_block(rounding):
+    for name, bits in inputs().items():
+        announce("nvfp4 %s %s" % (name, rounding))
+        out = nvfp4_quantize(to_gpu_bits(bits), axis="both", rounding=rounding, seed=6)
+        torch.cuda.synchronize()
+        for key in ("row", "col"):
+            rc, ri, ro = nvfp4_quantize_ref(bits, key, rounding=rounding, seed=6)
+            o = out[key]
+            assert_bytes_equal(o.outer.cpu().numpy().view(np.uint32), ro.view(np.uint32), "%s %s outer" % (name, key))
+            assert_bytes_equal(o.inner.cpu().numpy(), ri, "%s %s inner" % (name, key))
+            assert_bytes_equal(o.codes.cpu().numpy(), rc, "%s %s codes" % (name, key))
