@@ -16,7 +16,7 @@ before timing starts.
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
 with each family's achieved HBM GB/s or MFMA TFLOP/s; `mxnorm` times the fused
-MXNorm + row-wise cast launch apart from the step; `roofline` is the dominant
+MXNorm + row-wise cast launch apart from the step, `nvfp4` the double-block quantizer; `roofline` is the dominant
 kernel's; `cpu_baseline` is the CPU oracle on a bounded sample.
 """
 import argparse
@@ -136,6 +136,41 @@ def measure_mxnorm(tensors, dev, reps=30):
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def measure_block16(tensors, dev, reps=30):
+    """The NVFP4-style double-block quantizer (E4M3 per 16 values, float32 per 128), each axis timed apart.
+
+    The same six 8192 x 4096 tensors in rotation, RTNE; algorithmic bytes per launch: the bf16 read, codes,
+    inner and outer scales.
+    """
+    import torch
+    from block_scaled_fp4_hadamard_amd.api import nvfp4_quantize
+    names = ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"]
+    xs = [tensors[n] for n in names]
+    rows, cols = xs[0].shape
+    n = rows * cols
+    nbytes = 2 * n + n // 2 + n // 16 + 4 * (n // 128)
+    res = {"workload": "NVFP4-style double-block E2M1 RTNE cast, %dx%d bf16, %d tensors in rotation, each axis "
+                       "its own launch" % (rows, cols, len(xs)), "bytes_per_launch": nbytes}
+    stream = torch.cuda.current_stream(dev)
+    for axis in ("row", "col"):
+        outs = [nvfp4_quantize(x, axis=axis)[axis] for x in xs]
+        kw = lambda i: {"row_out": outs[i]} if axis == "row" else {"col_out": outs[i]}
+        for i, x in enumerate(xs):
+            nvfp4_quantize(x, axis=axis, **kw(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for j in range(reps):
+            i = j % len(xs)
+            nvfp4_quantize(xs[i], axis=axis, **kw(i))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[axis] = {"us_per_launch": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,6 +250,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom}
     mxnorm = measure_mxnorm(tensors, dev)
+    block16 = measure_block16(tensors, dev)
     qms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("quant"))
     gms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("gemm"))
     quant_gbs = step.quant_bytes / (qms * 1e-3) / 1e9
@@ -244,6 +280,7 @@ def main():
                  "ms_per_step": round(gms, 4)},
         "kernels": kernels,
         "mxnorm": mxnorm,
+        "nvfp4": block16,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -184,8 +184,11 @@ class NVTensor:
                              self.inner.stride(0), self.outer.data_ptr(), self.outer.stride(0))
 
 
-def nvfp4_quantize(x, axis="row", rounding="rtne", seed=0):
-    """NVFP4-style double-block quantization of a 2-D bf16 CUDA tensor; {"row": NVTensor, "col": NVTensor}."""
+def nvfp4_quantize(x, axis="row", rounding="rtne", seed=0, row_out=None, col_out=None):
+    """NVFP4-style double-block quantization of a 2-D bf16 CUDA tensor; {"row": NVTensor, "col": NVTensor}.
+
+    row_out / col_out reuse NVTensors from an earlier call of the same shape.
+    """
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     xb = _bits_view(x)
@@ -198,9 +201,9 @@ def nvfp4_quantize(x, axis="row", rounding="rtne", seed=0):
                         torch.empty((lines, k // 128), dtype=torch.float32, device=dev))
     out = {}
     if axis in ("row", "both"):
-        out["row"] = empty(rows, cols)
+        out["row"] = row_out if row_out is not None else empty(rows, cols)
     if axis in ("col", "both"):
-        out["col"] = empty(cols, rows)
+        out["col"] = col_out if col_out is not None else empty(cols, rows)
     rq = out["row"].c_struct() if "row" in out else None
     cq = out["col"].c_struct() if "col" in out else None
     st = _lib.mx_nvfp4_quantize(xb.data_ptr(), rows, cols, xb.stride(0), _lib.ROUND[rounding], _lib.AXIS[axis],

@@ -70,3 +70,33 @@ def test_nvfp4_double_block(rounding):
             assert_bytes_equal(o.outer.cpu().numpy().view(np.uint32), ro.view(np.uint32), "%s %s outer" % (name, key))
             assert_bytes_equal(o.inner.cpu().numpy(), ri, "%s %s inner" % (name, key))
             assert_bytes_equal(o.codes.cpu().numpy(), rc, "%s %s codes" % (name, key))
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_block16_multi_tile(rounding):
+    # several workgroup tiles with ragged edges: row segments of 4096 values (4112 = one more inner block),
+    # column bands of 128 rows x 256 columns (272 rows, 392 columns)
+    rng = np.random.default_rng(93)
+    cases = [((48, 4112), "row", False), ((272, 392), "col", False),
+             ((256, 4224), "both", True), ((256, 392), "col", True)]
+    for (rows, cols), axis, double in cases:
+        bits = synth.gradient(rows, cols, rng)
+        announce("block16 multi-tile %dx%d %s %s %s" % (rows, cols, axis, "double" if double else "mx16", rounding))
+        keys = ("row", "col") if axis == "both" else (axis,)
+        if double:
+            out = nvfp4_quantize(to_gpu_bits(bits), axis=axis, rounding=rounding, seed=8)
+            torch.cuda.synchronize()
+            for key in keys:
+                rc, ri, ro = nvfp4_quantize_ref(bits, key, rounding=rounding, seed=8)
+                o = out[key]
+                assert_bytes_equal(o.outer.cpu().numpy().view(np.uint32), ro.view(np.uint32), "%s outer" % key)
+                assert_bytes_equal(o.inner.cpu().numpy(), ri, "%s inner" % key)
+                assert_bytes_equal(o.codes.cpu().numpy(), rc, "%s codes" % key)
+        else:
+            out = quantize(to_gpu_bits(bits), axis=axis, rounding=rounding, seed=8, block=16)
+            torch.cuda.synchronize()
+            ref = quantize_ref(bits, axis, rounding=rounding, seed=8, block=16)
+            for key in keys:
+                c, s = qt_to_np(out[key])
+                assert_bytes_equal(s, ref[key][1], "%s scales" % key)
+                assert_bytes_equal(c, ref[key][0], "%s codes" % key)
