@@ -5,15 +5,19 @@
 //
 // MX16:   per 16 values, e = clamp(floor(log2 amax) - emax, -127, 127) as an
 //         E8M0 byte, then the MX cast (the 32-value kernel's rules).
-// Double: per 128 values s_o = RN32(amax128 / 2688) (float32; the float64
-//         quotient rounds to the same float32: amax / 21 for an 8-bit
-//         significand is exact or has a 6-bit periodic expansion, so it never
-//         lies on or within float64 rounding of a float32 midpoint); per 16
-//         values s_i = E4M3 nearest to amax16 / (6 s_o) (ties to even,
-//         saturating at 448; the float64 quotient lands on the same side of
-//         every E4M3 midpoint as the exact one); y = RN32(RN64(x * RN64(1 /
-//         (s_i s_o)))) cast to E2M1 at unit scale.  s_i = 0 leaves only the
-//         sign; an outer block with Inf/NaN gets s_o = NaN, inner 0x7F, codes 0.
+// Double: per 128 values s_o = RN32(amax128 / 2688) (float32); per 16 values
+//         s_i = E4M3 nearest to amax16 / (6 s_o) (ties to even, saturating at
+//         448); y = RN32(RN64(x * RN64(1 / (s_i s_o)))) cast to E2M1 at unit
+//         scale.  s_i = 0 leaves only the sign; an outer block with Inf/NaN
+//         gets s_o = NaN, inner 0x7F, codes 0.
+//
+// s_o is a product, RN32(amax * RN64(1/2688)): amax / 21 for an 8-bit
+// significand is exact or has a 6-bit periodic binary expansion, so it never
+// lies within a few float64 ulps of a float32 midpoint (checked for every
+// finite bf16).  The E4M3 argument stays a correctly rounded float64 division:
+// it can fall exactly on an E4M3 midpoint (amax16 6.375 under s_o 1), where a
+// product with an inexact reciprocal would break the tie either way; off the
+// midpoints it is at least 2^-32 of amax16 away from one.
 //
 // These scales are not what gfx950's scaled MFMA consumes (32-value blocks,
 // E8M0), so this is a quantizer only.
@@ -56,21 +60,19 @@ __device__ __forceinline__ uint32_t oct_max_pk(uint32_t v) {
   return v;
 }
 
-// nearest E4M3 code of q >= 0 (float64), ties to the even code, saturating at 448
+// nearest E4M3 code of q >= 0 (float64), ties to the even code, saturating at
+// 448.  Normal range: the float64 significand rounded to 3 bits in place (add
+// half an E4M3 ulp minus one, plus the kept lsb, then truncate; a carry bumps
+// the exponent).  Below 2^-6 the E4M3 step is 2^-9: k = q * 2^9 rounded by the
+// 2^52 add-subtract (k = 8 is the code of 2^-6).  Branch-free.
 __device__ __forceinline__ uint32_t e4m3_code(double q) {
-  if (!(q < 448.0)) return 0x7Eu;
-  int e2;
-  const double m = frexp(q, &e2);                 // q = m * 2^e2, m in [0.5, 1)
-  int E = e2 - 1;                                 // q in [2^E, 2^(E+1))
-  if (q == 0.0) return 0u;
-  if (E < -6) return (uint32_t)rint(ldexp(q, 9));   // subnormal: k * 2^-9; k = 8 is the code of 2^-6
-  uint32_t mant = (uint32_t)rint((ldexp(m, 1) - 1.0) * 8.0);
-  if (mant == 8u) {
-    mant = 0u;
-    ++E;
-  }
-  const uint32_t code = ((uint32_t)(E + 7) << 3) | mant;
-  return code > 0x7Eu ? 0x7Eu : code;
+  uint64_t b = (uint64_t)__double_as_longlong(q);
+  b += 0x0000FFFFFFFFFFFFull + ((b >> 49) & 1u);
+  const uint32_t hi = (uint32_t)(b >> 32);
+  const uint32_t normal = ((((hi >> 20) - 1016u) & 0x1Fu) << 3) | ((hi >> 17) & 7u);   // (E + 7) << 3 | m
+  const uint32_t sub = (uint32_t)((q * 512.0 + 0x1p52) - 0x1p52);
+  const uint32_t code = q < 0x1p-6 ? sub : normal;
+  return q < 448.0 ? code : 0x7Eu;
 }
 
 __device__ __forceinline__ double e4m3_value(uint32_t code) {
@@ -79,6 +81,12 @@ __device__ __forceinline__ double e4m3_value(uint32_t code) {
 }
 
 __device__ __forceinline__ double bf16_value(uint32_t mag) { return (double)__uint_as_float(mag << 16); }
+
+// a / b for tile indices (uniform): 32-bit when both fit
+__device__ __forceinline__ int64_t tile_div(int64_t a, int64_t b) {
+  if (((a | b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
 
 // One inner block of 16 values.  get(k) gives value k as float bits (the
 // bf16 pattern in the high half); amax16 / amax128 are the |x| maxima of the
@@ -122,24 +130,21 @@ __device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax
     }
   } else {
     zero_codes = amax128 >= 0x7F80u;
-    const float so = zero_codes ? __uint_as_float(0x7FC00000u) : (float)(bf16_value(amax128) / 2688.0);
+    const float so = zero_codes ? __uint_as_float(0x7FC00000u) : (float)(bf16_value(amax128) * (1.0 / 2688.0));
     so_out = so;
     uint32_t code = 0x7Fu;
     double r = 0.0;
     if (!zero_codes) {
       const double am = bf16_value(amax16);
-      code = (so > 0.0f && am > 0.0) ? e4m3_code(am / (6.0 * (double)so)) : 0u;
+      code = so > 0.0f ? e4m3_code(am / (6.0 * (double)so)) : 0u;
       const double d = e4m3_value(code) * (double)so;       // exact: 4 x 24 significant bits
       r = d > 0.0 ? 1.0 / d : 0.0;
     }
     scale = code;
+    // s_i = 0 gives r = 0, and x * 0 is the zero with x's sign (x finite here)
     float y[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t bits = get(k);
-      // s_i = 0: a signed zero keeps the sign
-      y[k] = r > 0.0 ? (float)((double)__uint_as_float(bits) * r) : __uint_as_float(bits & 0x80000000u);
-    }
+    for (int k = 0; k < 16; ++k) y[k] = (float)((double)__uint_as_float(get(k)) * r);
     if constexpr (ROUND == MX_ROUND_RTNE) {
       const float one = 1.0f;
 #pragma unroll
@@ -164,7 +169,7 @@ __device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax
 template <int MODE, int GRID, int ROUND>
 __device__ __forceinline__ void block16_row(const Block16Params& p, int64_t tile, int t) {
   const int64_t segs = (p.cols + kRowSpan - 1) / kRowSpan;
-  const int64_t row = tile / segs;
+  const int64_t row = tile_div(tile, segs);
   const int64_t pos0 = (tile - row * segs) * kRowSpan + 16 * t;
   if (pos0 >= p.cols) return;                     // whole inner (and, double block, outer) blocks only
   const uint16_t* src = p.x + row * p.ld_x + pos0;
@@ -190,15 +195,16 @@ __device__ __forceinline__ void block16_row(const Block16Params& p, int64_t tile
 template <int MODE, int GRID, int ROUND>
 __device__ __forceinline__ void block16_col(const Block16Params& p, int64_t tile, int t) {
   const int64_t ctiles = (p.cols + kColCols - 1) / kColCols;
-  const int64_t rt = tile / ctiles;
+  const int64_t rt = tile_div(tile, ctiles);
   const int lane = t & 63;
   const int64_t col = (tile - rt * ctiles) * kColCols + 64 * (t >> 6) + 8 * (lane >> 3);
   const int64_t row = rt * kColRows + 16 * (lane & 7);
   if (col >= p.cols || row >= p.rows) return;      // cols % 8 == 0; whole inner / outer blocks
+  const uint16_t* src = p.x + row * p.ld_x + col;
   uint32_t v[16][4];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint4 q = *(const uint4*)(p.x + (row + i) * p.ld_x + col);
+    const uint4 q = *(const uint4*)(src + i * p.ld_x);
     v[i][0] = q.x;
     v[i][1] = q.y;
     v[i][2] = q.z;
@@ -214,6 +220,9 @@ __device__ __forceinline__ void block16_col(const Block16Params& p, int64_t tile
     mo[d] = MODE == 1 ? oct_max_pk(m[d]) : 0u;
   }
   const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  uint8_t* const cbase = p.codes + col * p.ld_codes + row / 2;
+  uint8_t* const sbase = p.scales + col * p.ld_scales + row / 16;
+  float* const obase = p.outer + col * p.ld_outer + row / 128;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int d = j >> 1;
@@ -225,9 +234,9 @@ __device__ __forceinline__ void block16_col(const Block16Params& p, int64_t tile
     const int64_t line = col + j;
     const uint64_t ctr = ((uint64_t)line * (uint64_t)p.rows + (uint64_t)row) >> 2;
     const uint2 c = quant16<MODE, GRID, ROUND>(get, amax16, amax128, ctr, 1u, k0, k1, scale, so);
-    *(uint2*)(p.codes + line * p.ld_codes + row / 2) = c;
-    p.scales[line * p.ld_scales + row / 16] = (uint8_t)scale;
-    if (MODE == 1 && (lane & 7) == 0) p.outer[line * p.ld_outer + row / 128] = so;
+    *(uint2*)(cbase + j * p.ld_codes) = c;
+    sbase[j * p.ld_scales] = (uint8_t)scale;
+    if (MODE == 1 && (lane & 7) == 0) obase[j * p.ld_outer] = so;
   }
 }
 

@@ -100,3 +100,32 @@ def test_block16_multi_tile(rounding):
                 c, s = qt_to_np(out[key])
                 assert_bytes_equal(s, ref[key][1], "%s scales" % key)
                 assert_bytes_equal(c, ref[key][0], "%s codes" % key)
+
+
+def test_nvfp4_e4m3_sweep():
+    # every positive bf16 magnitude up to 2688 as an inner-block maximum under s_o = 1 (each outer block leads
+    # with 2688): s_i = E4M3 nearest to amax / 6 runs through every code, the subnormal range and exact ties
+    # (amax 6.375 gives 1.0625, halfway between 1 and 1.125)
+    mags = np.arange(1, 0x4528 + 1, dtype=np.uint16)           # 0x4528 = 2688.0
+    per_outer = 7
+    n_outer = (len(mags) + per_outer - 1) // per_outer
+    x = np.zeros((n_outer, 128), dtype=np.uint16)
+    rng = np.random.default_rng(94)
+    for i in range(n_outer):
+        x[i, 0] = 0x4528
+        for b, m in enumerate(mags[per_outer * i:per_outer * (i + 1)]):
+            x[i, 16 * (b + 1)] = m | (0x8000 if rng.random() < 0.5 else 0)
+            # fill the rest of the inner block with values at or below its maximum
+            x[i, 16 * (b + 1) + 1:16 * (b + 2)] = (rng.integers(0, int(m) + 1, 15) | (rng.integers(0, 2, 15) << 15)).astype(np.uint16)
+    rows = (n_outer + 7) // 8 * 8
+    bits = np.zeros((rows, 128), dtype=np.uint16)
+    bits[:n_outer] = x
+    announce("nvfp4 e4m3 sweep %dx128" % rows)
+    out = nvfp4_quantize(to_gpu_bits(bits), axis="row")["row"]
+    torch.cuda.synchronize()
+    rc, ri, ro = nvfp4_quantize_ref(bits, "row")
+    assert np.all(ro[:n_outer] == 1.0)
+    assert len(np.unique(ri[:n_outer, 1:])) == 127              # every finite E4M3 code
+    assert_bytes_equal(out.outer.cpu().numpy().view(np.uint32), ro.view(np.uint32), "outer")
+    assert_bytes_equal(out.inner.cpu().numpy(), ri, "inner")
+    assert_bytes_equal(out.codes.cpu().numpy(), rc, "codes")
