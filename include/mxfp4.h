@@ -119,7 +119,7 @@ typedef struct {
  *   grid       MX_GRID_E2M1 or MX_GRID_E1M2
  *   round      MX_ROUND_RTNE or MX_ROUND_SR (seed keys the Philox draws)
  *   axis       which outputs to write; row_out / col_out must be non-null for
- *              the requested ones (codes 16-byte aligned) and are ignored
+ *              the requested ones (codes 16-byte aligned, 8 with block 16) and are ignored
  *              otherwise
  * Both outputs of MX_AXIS_BOTH come from one pass over x.
  */
