@@ -129,3 +129,31 @@ def test_nvfp4_e4m3_sweep():
     assert_bytes_equal(out.outer.cpu().numpy().view(np.uint32), ro.view(np.uint32), "outer")
     assert_bytes_equal(out.inner.cpu().numpy(), ri, "inner")
     assert_bytes_equal(out.codes.cpu().numpy(), rc, "codes")
+
+
+def sample_lines(n, k, rng):
+    return np.unique(np.concatenate([rng.choice(n, k, replace=False), [0, n - 1]]))
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_block16_full_size_sampled(rounding):
+    # the size the benchmark times: 8192 x 4096 activations with outlier channels, and a gradient of the same
+    # shape; both axes of the double-block layout and of MX16, checked on sampled output lines
+    rng = np.random.default_rng(95)
+    for name, bits in (("activation", synth.activation(8192, 4096, rng)), ("gradient", synth.gradient(8192, 4096, rng))):
+        announce("block16 full size %s %s" % (name, rounding))
+        x = to_gpu_bits(bits)
+        nv = nvfp4_quantize(x, axis="both", rounding=rounding, seed=10)
+        mx = quantize(x, axis="both", rounding=rounding, seed=10, block=16)
+        torch.cuda.synchronize()
+        for key, n in (("row", 8192), ("col", 4096)):
+            ids = sample_lines(n, 48, rng)
+            rc, ri, ro = nvfp4_quantize_ref(bits, key, rounding=rounding, seed=10, lines=ids)
+            o = nv[key]
+            assert_bytes_equal(o.outer.cpu().numpy()[ids].view(np.uint32), ro.view(np.uint32), "%s %s outer" % (name, key))
+            assert_bytes_equal(o.inner.cpu().numpy()[ids], ri, "%s %s inner" % (name, key))
+            assert_bytes_equal(o.codes.cpu().numpy()[ids], rc, "%s %s codes" % (name, key))
+            ref = quantize_ref(bits, key, rounding=rounding, seed=10, block=16, lines=ids)[key]
+            c, s = qt_to_np(mx[key])
+            assert_bytes_equal(s[ids], ref[1], "%s %s mx16 scales" % (name, key))
+            assert_bytes_equal(c[ids], ref[0], "%s %s mx16 codes" % (name, key))
