@@ -491,17 +491,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Start copying a tile into an LDS buffer.  Wave w fills rows 8w .. 8w+7, two
 // rows (1 KB) per instruction: lane l writes stored piece l % 32 of row
 // 8w + 2i + l / 32, so it loads the global piece that the swizzle puts there.
-// Pieces outside the tensor are written as zeros instead.
+// That piece depends on the row only through r & 1 = l / 32 and (r >> 3) & 1
+// = w & 1, so it is the same for the four copies, whose offsets then step by
+// two rows.  Pieces outside the tensor are written as zeros instead; a tile
+// wholly inside takes no per-lane test.
 __device__ __forceinline__ void issue_tile(const QuantParams& p, int64_t row0, int64_t col0, int wave, int lane,
                                            uint8_t* buf) {
   const uint16_t* base = wave_uniform(p.x + row0 * p.ld_x + col0);
-  const int ps = lane & 31;
+  const int ps = lane & 31, hr = lane >> 5;
+  const int pg = ps ^ ((((ps >> 4) & 1) << 1) | hr | ((wave & 1) << 2));
+  const uint32_t off0 = (uint32_t)(((8 * wave + hr) * p.ld_x + 8 * pg) * 2);
+  const uint32_t step = (uint32_t)(4 * p.ld_x);                 // two rows of bf16, in bytes
+  const bool interior = row0 + kTileRows <= p.rows && col0 + kTileCols <= p.cols;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 8 * wave + 2 * i + (lane >> 5);
-    const int pg = ps ^ ((((ps >> 4) & 1) << 1) | (r & 1) | (((r >> 3) & 1) << 2));
-    if (row0 + r < p.rows && col0 + 8 * pg < p.cols)
-      dma16(base, (uint32_t)((r * p.ld_x + 8 * pg) * 2), lds_addr(buf + (8 * wave + 2 * i) * kRowBytes));
+    const int r = 8 * wave + 2 * i + hr;
+    if (interior || (row0 + r < p.rows && col0 + 8 * pg < p.cols))
+      dma16(base, off0 + (uint32_t)i * step, lds_addr(buf + (8 * wave + 2 * i) * kRowBytes));
     else
       *(uint4*)(buf + r * kRowBytes + ps * 16) = uint4{0u, 0u, 0u, 0u};
   }
@@ -625,6 +631,12 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
   const float c = HAD == 32 ? kInvSqrt32 : kInvSqrt16;
   if constexpr (DO_ROW) {
     const bool full_width = col0 + kTileCols <= p.cols;
+    const bool interior = full_width && row0 + kTileRows <= p.rows;
+    // the lane's output addresses for group 0; group g is 4g rows further
+    const int64_t rl = row0 + 8 * wave + (n >> 3);
+    uint8_t* const cbase = p.row_codes + rl * p.ld_row_codes + col0 / 2 + 16 * (n & 7) + 8 * hl;
+    uint8_t* const sbase = p.row_scales + rl * p.ld_row_scales + col0 / 32;
+    const uint64_t ctr0 = (((uint64_t)rl * (uint64_t)p.cols + (uint64_t)(col0 + 32 * (n & 7))) >> 2) + 4 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       __builtin_amdgcn_sched_barrier(0);
@@ -642,17 +654,21 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       float y[16];
       mfma_block_sums<PARTS>(ha, part, c, y);
       const int64_t row = row0 + r, c0 = col0 + 32 * k;
-      const bool valid = row < p.rows && c0 < p.cols;
+      const bool valid = interior || (row < p.rows && c0 < p.cols);
       uint32_t w[2];
-      const uint32_t byte = cast_half_block<GRID, ROUND>(
-          y, lane, (((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2) + 4 * hl, 0u, k0, k1, w);
-      if (valid) *(uint2*)(p.row_codes + row * p.ld_row_codes + c0 / 2 + 8 * hl) = uint2{w[0], w[1]};
-      store_row_scales(p.row_scales + row * p.ld_row_scales + col0 / 32, k, byte, wide_scales && full_width,
-                       valid && hl == 0);
+      // counter of the lane's first output: (row * cols + c0) / 4 + 4 hl, and cols % 8 == 0
+      const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)p.cols, 0u, k0, k1, w);
+      if (valid) *(uint2*)(cbase + 4 * g * p.ld_row_codes) = uint2{w[0], w[1]};
+      store_row_scales(sbase + 4 * g * p.ld_row_scales, k, byte, wide_scales && full_width, valid && hl == 0);
     }
   }
   if constexpr (DO_COL) {
     const int g16 = lane >> 4, s = lane & 15;
+    // the lane's output column in group 0 and its addresses; group g is 32 columns further
+    const int64_t cl = col0 + 64 * wave + n;
+    uint8_t* const ccbase = p.col_codes + cl * p.ld_col_codes + row0 / 2 + 8 * hl;
+    uint8_t* const csbase = p.col_scales + cl * p.ld_col_scales + row0 / 32;
+    const uint64_t cctr0 = (((uint64_t)cl * (uint64_t)p.rows + (uint64_t)row0) >> 2) + 4 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       __builtin_amdgcn_sched_barrier(0);
@@ -678,13 +694,14 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       }
       float y[16];
       mfma_block_sums<PARTS>(ha, part, c, y);
-      const int64_t cc = col0 + 64 * wave + 32 * g + n;
+      const int64_t cc = cl + 32 * g;
       uint32_t w[2];
-      const uint32_t byte = cast_half_block<GRID, ROUND>(
-          y, lane, (((uint64_t)cc * (uint64_t)p.rows + (uint64_t)row0) >> 2) + 4 * hl, 1u, k0, k1, w);
+      // counter: (cc * rows + row0) / 4 + 4 hl, and rows % 32 == 0 here
+      const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, cctr0 + (uint64_t)(8 * g) * (uint64_t)p.rows, 1u, k0,
+                                                         k1, w);
       if (cc < p.cols) {
-        *(uint2*)(p.col_codes + cc * p.ld_col_codes + row0 / 2 + 8 * hl) = uint2{w[0], w[1]};
-        if (hl == 0) p.col_scales[cc * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
+        *(uint2*)(ccbase + 32 * g * p.ld_col_codes) = uint2{w[0], w[1]};
+        if (hl == 0) csbase[32 * g * p.ld_col_scales] = (uint8_t)byte;
       }
     }
   }
