@@ -7,10 +7,12 @@ gradient are quantized along both axes (random-sign H32 rotation on every
 contraction axis, E8M0 block scales, E2M1 codes; RTNE for activations and
 weights, Philox stochastic rounding for gradients), then the Fprop, Dgrad and
 Wgrad MXFP4 GEMMs run with fp32 accumulation (bf16 Y and dX, fp32 dW).
-Inputs are seeded synthetic tensors of the real shapes, resident in HBM
-before timing starts.
+By default q/k/v and gate/up run as fused projections (qkv, gate_up: the
+same products and flops in 12 GEMMs and 12 quantizations); --unfused runs
+one GEMM per linear (21 GEMMs, 18 quantizations).  Inputs are seeded
+synthetic tensors of the real shapes, resident in HBM before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--unfused]
     python bench.py --calibrate-copy BYTES     (device copies of BYTES, for traffic-counter scaling)
 
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
@@ -44,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--unfused", action="store_true", help="one GEMM per linear instead of fused qkv and gate_up")
     return ap.parse_args()
 
 
@@ -194,7 +197,7 @@ def main():
     del host
     torch.cuda.synchronize()
     log("inputs ready in %.1f s" % (time.time() - t0))
-    step = LlamaBlockStep(tensors, Recipe(grid=args.grid))
+    step = LlamaBlockStep(tensors, Recipe(grid=args.grid, fuse=not args.unfused))
 
     for _ in range(args.warmup):
         step.run()
@@ -270,9 +273,13 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B block linears (q,k,v,o,gate,up,down) Fprop+Dgrad+Wgrad, "
-                               "%d tokens, RHT H32 on every contraction axis, SR on dY, %s" % (args.tokens, args.grid),
-                   "tokens": args.tokens, "d_model": 4096, "d_kv": 1024, "d_ffn": 14336, "gemms": 21,
-                   "quantize_launches": 18, "grid": args.grid, "gemm_tflop_per_step": round(step.flops / 1e12, 3),
+                               "%d tokens, RHT H32 on every contraction axis, SR on dY, %s%s" %
+                               (args.tokens, args.grid, ", one GEMM per linear" if args.unfused else
+                                ", q/k/v and gate/up as fused projections"),
+                   "tokens": args.tokens, "d_model": 4096, "d_kv": 1024, "d_ffn": 14336,
+                   "gemms": sum(1 for L in step.launches if L.flops),
+                   "quantize_launches": sum(1 for L in step.launches if not L.flops), "fused_projections":
+                   not args.unfused, "grid": args.grid, "gemm_tflop_per_step": round(step.flops / 1e12, 3),
                    "quant_gb_per_step": round(step.quant_bytes / 1e9, 3)},
         "quantize": {"GB/s": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4),
                      "ms_per_step": round(qms, 4)},

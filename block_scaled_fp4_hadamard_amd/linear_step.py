@@ -10,7 +10,14 @@ GEMM's contraction axis:
     Wgrad  dW = Q_col(dY) . Q_col(X)^T    M=out, N=in,  K=T    -> fp32
 
 so every tensor is quantized once along each of its two axes (one
-MX_AXIS_BOTH launch).  "Ripensare il Bias di Shrinkage ...", Metodologia 2:
+MX_AXIS_BOTH launch).  Linears that read the same input may run as one fused
+projection, as training frameworks run a Llama block: q, k, v as qkv and
+gate, up as gate_up, their weights stacked along the output features.  The
+fused GEMMs hold the same products (the fused Dgrad sums the parts' input
+gradients, which is the gradient the block needs), with the same flops and
+quantized element counts; column blocks and Hadamard chunks along the output
+features never straddle two parts, since every part's width is a multiple of
+32.  "Ripensare il Bias di Shrinkage ...", Metodologia 2:
 the UFP4 recipe puts the random Hadamard transform on all three GEMMs and
 stochastic rounding on dY only, round-to-nearest-even elsewhere.  Both
 operands of a GEMM are rotated along its contraction axis with the same sign
@@ -24,6 +31,20 @@ import torch
 
 from . import api
 from .synth import LLAMA_LINEARS, LLAMA_INPUT_OF
+
+# projections run as one GEMM each when fused: parts stacked along the output features
+FUSED_PROJECTIONS = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"), "down": ("down",)}
+
+
+def projections(fuse):
+    """{projection: its linears} of the block, fused or one per linear."""
+    return dict(FUSED_PROJECTIONS) if fuse else {lin: (lin,) for lin in LLAMA_LINEARS}
+
+
+def tensor_names(fuse):
+    """Every tensor the step quantizes, in the order that numbers their stochastic-rounding seeds."""
+    proj = projections(fuse)
+    return sorted(set(LLAMA_INPUT_OF.values())) + ["w_" + n for n in proj] + ["dy_" + n for n in proj]
 
 
 @dataclass
@@ -43,6 +64,7 @@ class Recipe:
     had_seed: int = 20250
     sr_on_dy: bool = True
     sr_seed_base: int = 5000
+    fuse: bool = True          # q/k/v and gate/up as fused projections
 
 
 def quant_bytes(rows, cols, axes=2):
@@ -67,11 +89,16 @@ class LlamaBlockStep:
         self.out = {}
         tokens = t["x_attn"].shape[0]
         self.launches = []
+        # the projections' stacked operands, built once outside any timed region
+        proj = projections(r.fuse)
+        self.operands = dict(t)
+        for name, parts in proj.items():
+            if len(parts) > 1:
+                self.operands["w_" + name] = torch.cat([t["w_" + p] for p in parts], dim=0).contiguous()
+                self.operands["dy_" + name] = torch.cat([t["dy_" + p] for p in parts], dim=1).contiguous()
         # quantize every input once (both axes), each weight, each gradient
-        names = sorted(set(LLAMA_INPUT_OF.values())) + ["w_" + n for n in LLAMA_LINEARS] + \
-            ["dy_" + n for n in LLAMA_LINEARS]
-        for ordinal, name in enumerate(names):
-            x = t[name]
+        for ordinal, name in enumerate(tensor_names(r.fuse)):
+            x = self.operands[name]
             rows, cols = x.shape
             qrow = api.empty_qtensor(rows, cols, dev, r.grid)
             qcol = api.empty_qtensor(cols, rows, dev, r.grid)
@@ -83,18 +110,20 @@ class LlamaBlockStep:
                   api.quantize(x, axis="both", grid=r.grid, rounding=rounding, seed=seed, had_n=r.had_n,
                                had_kind=r.had_kind, had_seed=r.had_seed, row_out=qrow, col_out=qcol))
             self.launches.append(Launch("quant." + rounding, "quantize " + name, fn, quant_bytes(rows, cols)))
-        for lin, (o, i) in LLAMA_LINEARS.items():
-            xq, wq, dq = self.q[LLAMA_INPUT_OF[lin]], self.q["w_" + lin], self.q["dy_" + lin]
+        for name, parts in proj.items():
+            o = sum(LLAMA_LINEARS[p][0] for p in parts)
+            i = LLAMA_LINEARS[parts[0]][1]
+            xq, wq, dq = self.q[LLAMA_INPUT_OF[parts[0]]], self.q["w_" + name], self.q["dy_" + name]
             y = torch.empty((tokens, o), dtype=torch.bfloat16, device=dev)
             dx = torch.empty((tokens, i), dtype=torch.bfloat16, device=dev)
             dw = torch.empty((o, i), dtype=torch.float32, device=dev)
-            self.out[lin] = {"y": y, "dx": dx, "dw": dw}
+            self.out[name] = {"y": y, "dx": dx, "dw": dw}
             flops = 2 * tokens * o * i
-            self.launches.append(Launch("gemm.bf16", "fprop " + lin,
+            self.launches.append(Launch("gemm.bf16", "fprop " + name,
                                         lambda a=xq["row"], b=wq["row"], c=y: api.gemm(a, b, out=c), 0, flops))
-            self.launches.append(Launch("gemm.bf16", "dgrad " + lin,
+            self.launches.append(Launch("gemm.bf16", "dgrad " + name,
                                         lambda a=dq["row"], b=wq["col"], c=dx: api.gemm(a, b, out=c), 0, flops))
-            self.launches.append(Launch("gemm.f32", "wgrad " + lin,
+            self.launches.append(Launch("gemm.f32", "wgrad " + name,
                                         lambda a=dq["col"], b=xq["col"], c=dw: api.gemm(a, b, out=c), 0, flops))
 
     def run(self):
@@ -112,6 +141,4 @@ class LlamaBlockStep:
 
 def sr_seed_of(recipe, name):
     """The stochastic-rounding seed LlamaBlockStep gives tensor `name`."""
-    names = sorted(set(LLAMA_INPUT_OF.values())) + ["w_" + n for n in LLAMA_LINEARS] + \
-        ["dy_" + n for n in LLAMA_LINEARS]
-    return recipe.sr_seed_base + names.index(name)
+    return recipe.sr_seed_base + tensor_names(recipe.fuse).index(name)

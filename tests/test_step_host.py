@@ -1,0 +1,50 @@
+"""The Llama-block step's schedule, fused and one GEMM per linear, built on the CPU (nothing launched)."""
+import torch
+
+from block_scaled_fp4_hadamard_amd.linear_step import LlamaBlockStep, Recipe, projections, sr_seed_of, tensor_names
+from block_scaled_fp4_hadamard_amd.synth import LLAMA_LINEARS, LLAMA_INPUT_OF
+
+
+def fake_block(tokens):
+    t = {}
+    dims = {"x_attn": 4096, "x_o": 4096, "x_mlp": 4096, "x_down": 14336}
+    for name, cols in dims.items():
+        t[name] = torch.zeros((tokens, cols), dtype=torch.int16)
+    for lin, (o, i) in LLAMA_LINEARS.items():
+        t["w_" + lin] = torch.zeros((o, i), dtype=torch.int16)
+        t["dy_" + lin] = torch.zeros((tokens, o), dtype=torch.int16)
+    return t
+
+
+def test_fused_and_unfused_steps_do_the_same_work():
+    t = fake_block(64)
+    fused, unfused = LlamaBlockStep(t, Recipe(fuse=True)), LlamaBlockStep(t, Recipe(fuse=False))
+    assert fused.flops == unfused.flops == 3 * 2 * 64 * sum(o * i for o, i in LLAMA_LINEARS.values())
+    assert fused.quant_bytes == unfused.quant_bytes
+    assert sum(1 for L in fused.launches if L.flops) == 12
+    assert sum(1 for L in unfused.launches if L.flops) == 21
+    assert sum(1 for L in fused.launches if not L.flops) == 12
+    assert sum(1 for L in unfused.launches if not L.flops) == 18
+
+
+def test_fused_operands_stack_the_parts():
+    t = fake_block(32)
+    for name in t:
+        t[name] = torch.randint(-2 ** 15, 2 ** 15, t[name].shape, dtype=torch.int16)
+    step = LlamaBlockStep(t, Recipe(fuse=True))
+    w, dy = step.operands["w_qkv"], step.operands["dy_qkv"]
+    assert w.shape == (6144, 4096) and dy.shape == (32, 6144)
+    assert torch.equal(w[4096:5120], t["w_k"]) and torch.equal(dy[:, 5120:], t["dy_v"])
+    assert step.operands["w_gate_up"].shape == (28672, 4096)
+    # every part of a fused projection reads the same input, and part widths are whole 32-blocks
+    for name, parts in projections(True).items():
+        assert len({LLAMA_INPUT_OF[p] for p in parts}) == 1
+        assert all(LLAMA_LINEARS[p][0] % 32 == 0 for p in parts)
+
+
+def test_seeds_follow_the_quantization_order():
+    for fuse in (True, False):
+        r = Recipe(fuse=fuse)
+        names = tensor_names(fuse)
+        assert [sr_seed_of(r, n) for n in names] == [r.sr_seed_base + k for k in range(len(names))]
+    assert sr_seed_of(Recipe(fuse=False), "dy_k") == 5000 + 4 + 7 + 1

@@ -73,7 +73,7 @@ def test_llama_k_projection_training_step(grid):
     """One linear of the Llama block (k: 1024 x 4096, 8192 tokens) through the block's recipe: random-sign H32
     on every operand's both axes, RTNE on X and W, stochastic rounding on dY; every quantized byte, then
     Fprop / Dgrad / Wgrad on sampled outputs."""
-    r = Recipe(grid=grid)
+    r = Recipe(grid=grid, fuse=False)
     d = synth.llama_block(only=["k"])
     x, w, dy = d["x_attn"], d["w_k"], d["dy_k"]
     dy_seed = sr_seed_of(r, "dy_k")
@@ -100,3 +100,37 @@ def test_llama_k_projection_training_step(grid):
         c_ref, g = gemm_of(ops, which, grid=grid, rows=rows, cols=cols)
         got = out[rows][:, cols].float().cpu().numpy()
         assert_gemm_close(got, c_ref, g, "%s %s" % (which, grid), bf16=bf16)
+
+
+def test_fused_projections_match_separate_linears():
+    """q/k/v and gate/up as fused projections: with RTNE on every operand each part's Fprop columns and Wgrad
+    rows equal the separate linears' GEMMs bit for bit (part widths are multiples of the 256-wide output tiles
+    and of the 32-value blocks, so every tile and block sees the same data in the same order)."""
+    from block_scaled_fp4_hadamard_amd.linear_step import LlamaBlockStep, FUSED_PROJECTIONS
+    from block_scaled_fp4_hadamard_amd.synth import LLAMA_LINEARS
+    announce("fused projections against separate linears")
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    tokens = 512
+
+    def bits(rows, cols, scale):
+        return (scale * torch.randn((rows, cols), device=dev, generator=g)).bfloat16().view(torch.int16)
+    t = {"x_attn": bits(tokens, 4096, 1.0), "x_o": bits(tokens, 4096, 1.0), "x_mlp": bits(tokens, 4096, 1.0),
+         "x_down": bits(tokens, 14336, 1.0)}
+    for lin, (o, i) in LLAMA_LINEARS.items():
+        t["w_" + lin] = bits(o, i, 0.02)
+        t["dy_" + lin] = bits(tokens, o, 1e-3)
+    fused = LlamaBlockStep(t, Recipe(fuse=True, sr_on_dy=False))
+    sep = LlamaBlockStep(t, Recipe(fuse=False, sr_on_dy=False))
+    fused.run()
+    sep.run()
+    torch.cuda.synchronize()
+    for name, parts in FUSED_PROJECTIONS.items():
+        y, dw = fused.out[name]["y"], fused.out[name]["dw"]
+        off = 0
+        for p in parts:
+            o = LLAMA_LINEARS[p][0]
+            assert torch.equal(y[:, off:off + o].view(torch.int16), sep.out[p]["y"].view(torch.int16)), p
+            assert torch.equal(dw[off:off + o].view(torch.int32), sep.out[p]["dw"].view(torch.int32)), p
+            off += o
