@@ -682,7 +682,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
           const int row = 16 * h + 8 * (g16 >> 1) + 4 * half + (s >> 2);
           typedef short v4s __attribute__((ext_vector_type(4)));
           const v4s q = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) uint8_t*)lds_addr(buf) +
+              (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) uint8_t*)(uint8_t*)buf +
                                                        row * kRowBytes + lds_col(col, row & 9)));
           d[2 * half] = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
           d[2 * half + 1] = (uint32_t)(uint16_t)q[2] | ((uint32_t)(uint16_t)q[3] << 16);
