@@ -218,12 +218,15 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
         transpose4(v, lane);
         const int64_t row = row0 + i * 32 + 8 * g + 4 * half + k;
         const int64_t col = col0 + j * 32 + 4 * quad;
+        // non-temporal: the output streams past the L2, which keeps the operand panels the next tiles read
         if constexpr (OUT == MX_OUT_F32) {
-          *(float4*)((float*)p.c + row * p.ldc + col) = float4{v[0], v[1], v[2], v[3]};
+          typedef float f4v __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, (f4v*)((float*)p.c + row * p.ldc + col));
         } else {
           const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
           const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-          *(uint2*)((uint16_t*)p.c + row * p.ldc + col) = uint2{lo, hi2};
+          typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(u2v{lo, hi2}, (u2v*)((uint16_t*)p.c + row * p.ldc + col));
         }
       }
 }
