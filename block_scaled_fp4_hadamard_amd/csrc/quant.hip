@@ -472,9 +472,13 @@ constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
 
 // global -> LDS copy of 16 bytes per lane (gfx950 LDS DMA): lane l's bytes
-// land at LDS address m0 + 16 l.  The s_nop covers the M0 write hazard.
+// land at LDS address m0 + 16 l.  The s_nop covers the M0 write hazard.  The
+// input is read once, so the copy is non-temporal; so are the row-wise
+// outputs, whole lines written once.  The column-wise outputs are not: their
+// 16-byte pieces of a line meet in L2, and streaming them past it made the
+// kernel 1.6x slower.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 // a pointer that is the same in every lane, moved to SGPRs
@@ -525,7 +529,8 @@ __device__ __forceinline__ void store_row_scales(uint8_t* dst, int k, uint32_t b
   const uint32_t hi = (uint32_t)__shfl_xor((int)v, 4);
   if (!active) return;
   if (wide) {
-    if (k == 0) *(uint2*)dst = uint2{v, hi};
+    typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+    if (k == 0) __builtin_nontemporal_store(u2v{v, hi}, (u2v*)dst);
   } else {
     dst[k] = (uint8_t)byte;
   }
@@ -658,7 +663,8 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       uint32_t w[2];
       // counter of the lane's first output: (row * cols + c0) / 4 + 4 hl, and cols % 8 == 0
       const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)p.cols, 0u, k0, k1, w);
-      if (valid) *(uint2*)(cbase + 4 * g * p.ld_row_codes) = uint2{w[0], w[1]};
+      typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+      if (valid) __builtin_nontemporal_store(u2v{w[0], w[1]}, (u2v*)(cbase + 4 * g * p.ld_row_codes));
       store_row_scales(sbase + 4 * g * p.ld_row_scales, k, byte, wide_scales && full_width, valid && hl == 0);
     }
   }
