@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(64 * kNormWaves) mxnorm_kernel(const MxNormPar
       uint32_t word;
       const uint32_t byte = cast8<GRID, ROUND>(v[ch], rho, row * p.cols + col, k0, k1, word);
       if (col < p.cols) {
-        *(uint32_t*)(p.codes + row * p.ld_codes + col / 2) = word;
+        __builtin_nontemporal_store(word, (uint32_t*)(p.codes + row * p.ld_codes + col / 2));   // written once
         if ((lane & 3) == 0) p.scales[row * p.ld_scales + col / 32] = (uint8_t)byte;
       }
     }

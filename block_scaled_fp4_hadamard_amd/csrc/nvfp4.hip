@@ -45,6 +45,13 @@ constexpr int kRowSpan = 16 * kB16Threads;     // values of a row per workgroup 
 constexpr int kColRows = 128, kColCols = 256;  // column-axis workgroup tile
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes read once: a non-temporal load
+__device__ __forceinline__ uint4 load_once(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return uint4{v.x, v.y, v.z, v.w};
+}
 
 // lane-wise max of two pairs of 16-bit magnitudes
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
@@ -173,7 +180,8 @@ __device__ __forceinline__ void block16_row(const Block16Params& p, int64_t tile
   const int64_t pos0 = (tile - row * segs) * kRowSpan + 16 * t;
   if (pos0 >= p.cols) return;                     // whole inner (and, double block, outer) blocks only
   const uint16_t* src = p.x + row * p.ld_x + pos0;
-  const uint4 a = *(const uint4*)src, b = *(const uint4*)(src + 8);
+  // read once: non-temporal loads (and row-wise code stores, whole lines written once)
+  const uint4 a = load_once(src), b = load_once(src + 8);
   const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t m = v[0] & 0x7FFF7FFFu;
 #pragma unroll
@@ -186,7 +194,8 @@ __device__ __forceinline__ void block16_row(const Block16Params& p, int64_t tile
   const uint64_t ctr = ((uint64_t)row * (uint64_t)p.cols + (uint64_t)pos0) >> 2;
   const uint2 c = quant16<MODE, GRID, ROUND>(get, amax16, amax128, ctr, 0u, (uint32_t)p.seed,
                                             (uint32_t)(p.seed >> 32), scale, so);
-  *(uint2*)(p.codes + row * p.ld_codes + pos0 / 2) = c;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2{c.x, c.y}, (u32x2*)(p.codes + row * p.ld_codes + pos0 / 2));
   p.scales[row * p.ld_scales + pos0 / 16] = (uint8_t)scale;
   if (MODE == 1 && (t & 7) == 0) p.outer[row * p.ld_outer + pos0 / 128] = so;
 }
@@ -204,7 +213,7 @@ __device__ __forceinline__ void block16_col(const Block16Params& p, int64_t tile
   uint32_t v[16][4];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint4 q = *(const uint4*)(src + i * p.ld_x);
+    const uint4 q = load_once(src + i * p.ld_x);
     v[i][0] = q.x;
     v[i][1] = q.y;
     v[i][2] = q.z;
