@@ -331,6 +331,16 @@ __device__ __forceinline__ void mfma_quarter(const Frags& f, v16f (&acc)[4][2], 
   for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]));
 }
 
+// First row (or column) of tile t of a dimension of size n >= 256: the last
+// tile of a ragged dimension is moved back to end at n, so every copy reads
+// rows inside the operand and every store lands inside C.  The rows it shares
+// with the tile before are computed twice by the same MFMA sequence, and
+// both writes carry the same bits.
+__device__ __forceinline__ int64_t tile_origin(int t, int tile, int64_t n) {
+  const int64_t o = (int64_t)t * tile;
+  return o + tile <= n ? o : n - tile;
+}
+
 // Persistent: one workgroup per CU walks its tiles (round r of the XCD-grouped
 // order: group r*8 + xcd, member = this workgroup's index on its XCD) as one
 // continuous stream of K steps, so the DMA lookahead runs across tile
@@ -403,7 +413,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   // DMA of K step kt of tile (tbm, tbn) into stage st, by the waves of parity kt % 2
   auto issue = [&](int tbm, int tbn, int kt, int st) {
     if ((wave >> 2) != (kt & 1)) return;
-    const int64_t m0 = (int64_t)tbm * kBM, n0 = (int64_t)tbn * kBN;
+    const int64_t m0 = tile_origin(tbm, kBM, p.M), n0 = tile_origin(tbn, kBN, p.N);
     const uint8_t* abase = wave_uniform(p.a_codes + m0 * p.lda_codes);
     const uint8_t* bbase = wave_uniform(p.b_codes + n0 * p.ldb_codes);
     const uint8_t* sabase = wave_uniform(p.a_scales + m0 * p.lda_scales);
@@ -478,7 +488,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       mfma_quarter<GRID, 2>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile_wide<OUT, 4, 2>(p, (int64_t)bm * kBM + r0, (int64_t)bn * kBN + c0, lane, acc);
+    store_tile_wide<OUT, 4, 2>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc);
     if (rn >= w.rounds) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -574,10 +584,11 @@ hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStre
   tm.groups = tm.groups_m * groups_n;
   const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
   const dim3 g((unsigned)wgs);
-  // the DMA path needs whole tiles, whole 256-element K steps (at least two),
-  // 4-byte aligned scale rows and output rows aligned for its 16-byte (fp32)
-  // or 8-byte (bf16) stores
-  const bool full = (p.M % kBM == 0) && (p.N % kBN == 0) && (p.K % 256 == 0) && (p.K >= 512) &&
+  // the DMA path needs at least one whole tile along M and N (a ragged last
+  // tile is moved back to end at the edge), whole 256-element K steps (at
+  // least two), 4-byte aligned scale rows, and output rows and columns
+  // aligned for its 16-byte (fp32) or 8-byte (bf16) stores
+  const bool full = (p.M >= kBM) && (p.N >= kBN) && (p.N % 4 == 0) && (p.K % 256 == 0) && (p.K >= 512) &&
                     ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.b_scales % 4 == 0) &&
                     (p.lda_scales % 4 == 0) && (p.ldb_scales % 4 == 0) &&
                     (p.ldc % 4 == 0) && ((uintptr_t)p.c % (out_kind == MX_OUT_F32 ? 16 : 8) == 0);

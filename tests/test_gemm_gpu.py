@@ -69,6 +69,39 @@ def test_whole_tile_path_both_outputs(grid, m, n, k):
     assert np.array_equal(c16, want)
 
 
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("m,n,k", [(300, 520, 512), (1000, 260, 1024), (257, 1028, 768), (640, 256, 2048)])
+def test_whole_tile_path_ragged_edges(grid, m, n, k):
+    """Ragged M and N on the whole-tile path: the last tile along each is moved back to end at the edge and
+    recomputes rows and columns of the tile before it; every output against the oracle, bf16 the RNE cast of
+    fp32 (so the doubly written rows carry the same bits either way)."""
+    announce("gemm ragged whole-tile %s %dx%dx%d" % (grid, m, n, k))
+    rng = np.random.default_rng(m * 5 + n + k)
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c32 = run_gemm(a, b, grid, torch.float32)
+    c16 = run_gemm(a, b, grid, torch.bfloat16)
+    c_ref, g = gemm_ref(*a, *b, k, grid)
+    assert_gemm_close(c32, c_ref, g, "ragged whole-tile fp32 %s" % grid)
+    want = torch.from_numpy(c32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(c16, want)
+
+
+def test_ragged_tokens_full_size_sampled():
+    """8000 tokens (not a multiple of the 256-row tile) through Fprop shapes, 8000x4096x4096, on sampled
+    outputs including the last rows, which the moved-back last tile computes."""
+    announce("gemm ragged tokens 8000x4096x4096")
+    rng = np.random.default_rng(8000)
+    m, n, k = 8000, 4096, 4096
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c = run_gemm(a, b, "e2m1", torch.float32)
+    rows = np.unique(np.concatenate([rng.choice(m, 40, replace=False), np.arange(m - 260, m, 13), [0, m - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(n, 40, replace=False), [0, n - 1]]))
+    c_ref, g = gemm_ref(a[0][rows], a[1][rows], b[0][cols], b[1][cols], k, "e2m1")
+    assert_gemm_close(c[rows][:, cols], c_ref, g, "ragged tokens")
+
+
 def test_tiny_workload_end_to_end():
     """256x256 A (2 outlier columns) times W^T: oracle-quantized operands, GPU bytes must match."""
     d = synth.tiny()
