@@ -52,8 +52,11 @@ def _bits_view(x):
 
 
 def empty_qtensor(lines, k, device, grid="e2m1", block=32):
-    return QTensor(torch.empty((lines, k // 2), dtype=torch.uint8, device=device),
-                   torch.empty((lines, k // block), dtype=torch.uint8, device=device), grid)
+    """An output operand; scale rows are padded to a multiple of 4 bytes, which the GEMM's copy path needs
+    (the padding is never read as data)."""
+    nb = k // block
+    scales = torch.empty((lines, (nb + 3) // 4 * 4), dtype=torch.uint8, device=device)[:, :nb]
+    return QTensor(torch.empty((lines, k // 2), dtype=torch.uint8, device=device), scales, grid)
 
 
 def quantize(x, axis="row", grid="e2m1", rounding="rtne", seed=0, had_n=0, had_kind="det", had_seed=0,

@@ -283,8 +283,12 @@ struct Frags {
 // fragments of K quarter q (64 deep) for the wave's 4 x 2 tiles.  Tile rows
 // start at multiples of 32, so a lane's swizzled slot depends only on its row
 // within the tile: one per-lane offset per quarter, the tiles are immediates.
+// vb: whole 32-value blocks of this K step inside K (8 but in a ragged last
+// step).  A lane's block in quarter q is 2q + half; past the edge its codes
+// are zeros in LDS and its scale dwords may be stale or never copied, so it
+// takes a stand-in scale (all bytes 127): the products stay exact zeros.
 __device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const uint8_t* b, const uint32_t* sa,
-                                             const uint32_t* sb, int q, int r0, int c0, int lane) {
+                                             const uint32_t* sb, int q, int r0, int c0, int lane, int vb) {
   const int half = lane >> 5, lrow = lane & 31;
   const int off = lrow * kRowBytes + swz8(lrow, 2 * q + half);
 #pragma unroll
@@ -296,6 +300,14 @@ __device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const u
   for (int j = 0; j < 2; ++j) {
     f.b[j] = *(const uint4*)(b + (c0 + 32 * j) * kRowBytes + off);
     f.sb[j] = sb[(q >> 1) * kBN + c0 + 32 * j + lrow];
+  }
+  if (vb < 8) {
+    if (2 * q + half >= vb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.sa[i] = 0x7F7F7F7Fu;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.sb[j] = 0x7F7F7F7Fu;
+    }
   }
 }
 
@@ -364,7 +376,9 @@ __device__ __forceinline__ int next_round(const TileMap& tm, const Walk& w, int 
   return w.rounds;
 }
 
-template <int GRID, int OUT>
+// RK: K is not a multiple of 256 (a ragged last step); a separate instance, so
+// that the whole-step kernel carries none of its register cost
+template <int GRID, int OUT, bool RK>
 __global__ void __launch_bounds__(kFullThreads, 1)
 gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kFullStageBytes];
@@ -383,7 +397,9 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int r0 = wm * 128, c0 = wn * 64;
-  const int nk = (int)(p.K / 256);
+  const int nk = (int)((p.K + 255) / 256);
+  const int vb_last = RK ? (int)((p.K % 256) / 32) : 8;   // blocks in the last step
+  auto blocks_in = [&](int kt) { return RK && kt == nk - 1 ? vb_last : 8; };
 
   // DMA: one instruction moves 64 lanes x 16 B = 1 KB = 8 rows of 128 B; lane
   // i -> row +i/8, LDS slot i%8, which must hold global piece (i%8) ^
@@ -419,17 +435,45 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
     const uint8_t* sabase = wave_uniform(p.a_scales + m0 * p.lda_scales);
     const uint8_t* sbbase = wave_uniform(p.b_scales + n0 * p.ldb_scales);
     const uint32_t kb = (uint32_t)kt * kRowBytes;
+    const int vb = blocks_in(kt);
+    if (vb == 8) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        dma16_off(abase, oa[4 * h + c] + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
-        dma16_off(bbase, ob[4 * h + c] + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+        for (int c = 0; c < 4; ++c) {
+          dma16_off(abase, oa[4 * h + c] + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+          dma16_off(bbase, ob[4 * h + c] + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+        }
+      dma4_off(sabase, osa + 8 * kt, lSA + st * (2 * kBM * 4));
+      dma4_off(sabase, osa + 8 * kt + 4, lSA + st * (2 * kBM * 4) + kBM * 4);
+      dma4_off(sbbase, osb + 8 * kt, lSB + st * (2 * kBN * 4));
+      dma4_off(sbbase, osb + 8 * kt + 4, lSB + st * (2 * kBN * 4) + kBN * 4);
+    } else {
+      // ragged last step: a lane copies its piece (block (lane % 8) ^ swizzle of its row) only if the block
+      // lies inside K, and writes zeros in its place otherwise, so nothing past the row's K edge is read.  A
+      // scale dword is copied if it holds a block inside K: it then ends within the scale row, whose stride
+      // is a multiple of 4 bytes.  Blocks past the edge take a stand-in scale when read (load_quarter).
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int gp = (lane & 7) ^ (4 * (c & 1) + (lane >> 4));
+          const int rowoff = (32 * (wave & 3) + 128 * h + 8 * c) * kRowBytes + 16 * lane;
+          if (gp < vb) {
+            dma16_off(abase, oa[4 * h + c] + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+            dma16_off(bbase, ob[4 * h + c] + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+          } else {
+            *(uint4*)(&sA[st][rowoff]) = uint4{0u, 0u, 0u, 0u};
+            *(uint4*)(&sB[st][rowoff]) = uint4{0u, 0u, 0u, 0u};
+          }
+        }
+      dma4_off(sabase, osa + 8 * kt, lSA + st * (2 * kBM * 4));
+      dma4_off(sbbase, osb + 8 * kt, lSB + st * (2 * kBN * 4));
+      if (vb > 4) {
+        dma4_off(sabase, osa + 8 * kt + 4, lSA + st * (2 * kBM * 4) + kBM * 4);
+        dma4_off(sbbase, osb + 8 * kt + 4, lSB + st * (2 * kBN * 4) + kBN * 4);
       }
-    dma4_off(sabase, osa + 8 * kt, lSA + st * (2 * kBM * 4));
-    dma4_off(sabase, osa + 8 * kt + 4, lSA + st * (2 * kBM * 4) + kBM * 4);
-    dma4_off(sbbase, osb + 8 * kt, lSB + st * (2 * kBN * 4));
-    dma4_off(sbbase, osb + 8 * kt + 4, lSB + st * (2 * kBN * 4) + kBN * 4);
+    }
   };
 
   v16f acc[4][2];
@@ -450,7 +494,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   __builtin_amdgcn_s_barrier();
   if (nk > 1) issue(bm, bn, 1, 1);
   else if (rn < w.rounds) issue(nbm, nbn, 0, 1);
-  load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane);
+  load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0));
   int st = 0;
   for (;;) {
     for (int kt = 0; kt < nk; ++kt) {
@@ -460,15 +504,16 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       const uint32_t* sb = sSB[st];
       // sched_barrier keeps each phase where it is written: without it the
       // scheduler hoists every quarter's reads to the top and runs out of VGPRs
-      load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane);
+      const int vb = blocks_in(kt);
+      load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane, vb);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 0>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
-      load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane);
+      load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane, vb);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 2>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
-      load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane);
+      load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane, vb);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 0>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
@@ -482,7 +527,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
         if (kt + 2 < nk) issue(bm, bn, kt + 2, st);
         else if (rn < w.rounds && kt + 2 - nk < nk) issue(nbm, nbn, kt + 2 - nk, st);
         st ^= 1;
-        load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane);
+        load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0));
       }
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 2>(f1, acc, shift);
@@ -568,8 +613,9 @@ static void launch_kind(const GemmParams& p, const TileMap& tm, bool full, dim3 
   if (full) {
     // one workgroup per CU: 8 XCDs x 32 members; round r deals group r*8+xcd
     const int rounds = (tm.groups + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT>), dim3(kXcds * kGroupM * kGroupN), dim3(kFullThreads), 0, s, p,
-                       tm, rounds);
+    const dim3 g(kXcds * kGroupM * kGroupN), b(kFullThreads);
+    if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false>), g, b, 0, s, p, tm, rounds);
+    else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true>), g, b, 0, s, p, tm, rounds);
   } else {
     hipLaunchKernelGGL((gemm_general_kernel<GRID, OUT>), g, dim3(kGemmThreads), 0, s, p, tm);
   }
@@ -585,10 +631,11 @@ hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStre
   const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
   const dim3 g((unsigned)wgs);
   // the DMA path needs at least one whole tile along M and N (a ragged last
-  // tile is moved back to end at the edge), whole 256-element K steps (at
-  // least two), 4-byte aligned scale rows, and output rows and columns
-  // aligned for its 16-byte (fp32) or 8-byte (bf16) stores
-  const bool full = (p.M >= kBM) && (p.N >= kBN) && (p.N % 4 == 0) && (p.K % 256 == 0) && (p.K >= 512) &&
+  // tile is moved back to end at the edge), at least two 256-element K steps
+  // (a ragged last step is zero-filled), 4-byte aligned scale rows, and
+  // output rows and columns aligned for its 16-byte (fp32) or 8-byte (bf16)
+  // stores
+  const bool full = (p.M >= kBM) && (p.N >= kBN) && (p.N % 4 == 0) && (p.K >= 512) &&
                     ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.b_scales % 4 == 0) &&
                     (p.lda_scales % 4 == 0) && (p.ldb_scales % 4 == 0) &&
                     (p.ldc % 4 == 0) && ((uintptr_t)p.c % (out_kind == MX_OUT_F32 ? 16 : 8) == 0);

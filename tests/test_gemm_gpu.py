@@ -87,15 +87,51 @@ def test_whole_tile_path_ragged_edges(grid, m, n, k):
     assert np.array_equal(c16, want)
 
 
-def test_ragged_tokens_full_size_sampled():
-    """8000 tokens (not a multiple of the 256-row tile) through Fprop shapes, 8000x4096x4096, on sampled
-    outputs including the last rows, which the moved-back last tile computes."""
-    announce("gemm ragged tokens 8000x4096x4096")
-    rng = np.random.default_rng(8000)
-    m, n, k = 8000, 4096, 4096
+def padded_qtensor(op, grid, fill=0xFF):
+    """A GPU operand whose scale rows are padded to a multiple of 4 bytes, the padding set to `fill` (0xFF is
+    the NaN scale: any use of it would poison the products)."""
+    codes, scales = op
+    lines, nb = scales.shape
+    buf = torch.full((lines, (nb + 3) // 4 * 4), fill, dtype=torch.uint8)
+    buf[:, :nb] = torch.from_numpy(scales)
+    return QTensor(torch.from_numpy(codes).cuda(), buf.cuda()[:, :nb], grid)
+
+
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("m,n,k", [(512, 512, 544), (300, 520, 672), (256, 1028, 896), (640, 512, 1248),
+                                   (768, 256, 4000)])
+def test_whole_tile_path_ragged_k(grid, m, n, k):
+    """K not a multiple of 256 on the whole-tile path (scale rows padded to 4 bytes, the padding NaN scales):
+    the last K step copies only the blocks inside K, zero-fills the rest and gives them a stand-in scale.
+    Last steps of 1, 4, 5 and 7 blocks; fp32 against the oracle, bf16 the RNE cast of fp32."""
+    announce("gemm ragged K %s %dx%dx%d" % (grid, m, n, k))
+    rng = np.random.default_rng(m + 3 * n + 7 * k)
     a = random_operand(rng, m, k)
     b = random_operand(rng, n, k)
-    c = run_gemm(a, b, "e2m1", torch.float32)
+    qa, qb = padded_qtensor(a, grid), padded_qtensor(b, grid)
+    assert qa.scales.stride(0) % 4 == 0
+    c32 = gemm(qa, qb, out_dtype=torch.float32)
+    c16 = gemm(qa, qb, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    c32, c16 = c32.cpu().numpy(), c16.float().cpu().numpy()
+    c_ref, g = gemm_ref(*a, *b, k, grid)
+    assert np.all(np.isfinite(c32))
+    assert_gemm_close(c32, c_ref, g, "ragged K fp32 %s" % grid)
+    want = torch.from_numpy(c32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(c16, want)
+
+
+@pytest.mark.parametrize("m,n,k", [(8000, 4096, 4096), (4096, 4096, 8000)])
+def test_ragged_tokens_full_size_sampled(m, n, k):
+    """8000 tokens (not a multiple of 256) at full size on sampled outputs: as M (Fprop / Dgrad shapes; the
+    last rows come from the moved-back last tile) and as K (Wgrad; a ragged last K step of 64 values)."""
+    announce("gemm ragged tokens %dx%dx%d" % (m, n, k))
+    rng = np.random.default_rng(m + k)
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c = gemm(padded_qtensor(a, "e2m1"), padded_qtensor(b, "e2m1"), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c = c.cpu().numpy()
     rows = np.unique(np.concatenate([rng.choice(m, 40, replace=False), np.arange(m - 260, m, 13), [0, m - 1]]))
     cols = np.unique(np.concatenate([rng.choice(n, 40, replace=False), [0, n - 1]]))
     c_ref, g = gemm_ref(a[0][rows], a[1][rows], b[0][cols], b[1][cols], k, "e2m1")
