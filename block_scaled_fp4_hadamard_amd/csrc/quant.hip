@@ -518,15 +518,43 @@ __device__ __forceinline__ void issue_tile(const QuantParams& p, int64_t row0, i
 }
 
 
+// DPP lane exchanges within rows of 16 lanes: l ^ 1, l ^ 2 (quad permutes),
+// and 7 - l within each group of 8 (half-row mirror)
+__device__ __forceinline__ uint32_t dpp_x1(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_x2(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_hm(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t dpp_m(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false); }
+
+// max / min over the whole wave (every lane active): the 16-lane rows by DPP,
+// then the four rows' first lanes
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, dpp_x1(v));
+  v = max(v, dpp_x2(v));
+  v = max(v, dpp_hm(v));
+  v = max(v, dpp_m(v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  v = min(v, dpp_x1(v));
+  v = min(v, dpp_x2(v));
+  v = min(v, dpp_hm(v));
+  v = min(v, dpp_m(v));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 // Scale bytes of 8 consecutive blocks of a row, held by lanes 8a .. 8a+7
 // (k = lane % 8): with 8-byte aligned scale rows and all 8 blocks inside the
 // tensor, the lane with k == 0 writes all 8 at once.  All lanes of the wave
-// must call this (the gather is a cross-lane exchange).
+// must call this (the gather is a cross-lane exchange: after the two quad
+// steps every lane holds its quad's four bytes, and the half-row mirror
+// brings the other quad's).
 __device__ __forceinline__ void store_row_scales(uint8_t* dst, int k, uint32_t byte, bool wide, bool active) {
   uint32_t v = byte << (8 * (k & 3));
-  v |= (uint32_t)__shfl_xor((int)v, 1);
-  v |= (uint32_t)__shfl_xor((int)v, 2);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)v, 4);
+  v |= dpp_x1(v);
+  v |= dpp_x2(v);
+  const uint32_t hi = dpp_hm(v);
   if (!active) return;
   if (wide) {
     typedef unsigned int u2v __attribute__((ext_vector_type(2)));
@@ -773,13 +801,8 @@ quant_kernel(const QuantParams p) {
         mn2 = __builtin_elementwise_min(mn2, m - (us2){1, 1});  // zero wraps to 0xFFFF: ignored
       }
     }
-    uint32_t mx = max((uint32_t)mx2.x, (uint32_t)mx2.y);
-    uint32_t mn = min((uint32_t)mn2.x, (uint32_t)mn2.y);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    }
+    uint32_t mx = wave_max(max((uint32_t)mx2.x, (uint32_t)mx2.y));
+    uint32_t mn = wave_min(min((uint32_t)mn2.x, (uint32_t)mn2.y));
     if (lane == 0) {
       red[wave] = mx;
       red[4 + wave] = mn;
