@@ -81,7 +81,7 @@ def load_traffic(family):
         return None
 
 
-def cpu_baseline(tokens=2048):
+def cpu_baseline(tokens=4096):
     """The oracle on one q-projection linear (4096x4096) with `tokens` tokens: the same
     quantization recipe and the three GEMMs, timed on this host's cores."""
     import numpy as np

@@ -37,7 +37,7 @@ def kernel_family(name):
     m = re.search(r"quant_kernel<(\d+), (\d+), (\d+),", name)
     if m:
         return "quant.sr" if m.group(3) == "1" else "quant.rtne"
-    m = re.search(r"gemm_\w*kernel<(\d+), (\d+)>", name)
+    m = re.search(r"gemm_\w*kernel<(\d+), (\d+)(, (true|false))?>", name)
     if m:
         return "gemm.bf16" if m.group(2) == "1" else "gemm.f32"
     if "mxnorm_kernel" in name:
