@@ -288,18 +288,20 @@ struct Frags {
 // are zeros in LDS and its scale dwords may be stale or never copied, so it
 // takes a stand-in scale (all bytes 127): the products stay exact zeros.
 __device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const uint8_t* b, const uint32_t* sa,
-                                             const uint32_t* sb, int q, int r0, int c0, int lane, int vb) {
+                                             const uint32_t* sb, int q, int r0, int c0, int lane, int vb,
+                                             const Frags& prev) {
   const int half = lane >> 5, lrow = lane & 31;
   const int off = lrow * kRowBytes + swz8(lrow, 2 * q + half);
+  // quarters 1 and 3 use the same scale dword as 0 and 2: taken from the previous quarter's fragments
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     f.a[i] = *(const uint4*)(a + (r0 + 32 * i) * kRowBytes + off);
-    f.sa[i] = sa[(q >> 1) * kBM + r0 + 32 * i + lrow];
+    f.sa[i] = (q & 1) ? prev.sa[i] : sa[(q >> 1) * kBM + r0 + 32 * i + lrow];
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     f.b[j] = *(const uint4*)(b + (c0 + 32 * j) * kRowBytes + off);
-    f.sb[j] = sb[(q >> 1) * kBN + c0 + 32 * j + lrow];
+    f.sb[j] = (q & 1) ? prev.sb[j] : sb[(q >> 1) * kBN + c0 + 32 * j + lrow];
   }
   if (vb < 8) {
     if (2 * q + half >= vb) {
@@ -494,7 +496,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   __builtin_amdgcn_s_barrier();
   if (nk > 1) issue(bm, bn, 1, 1);
   else if (rn < w.rounds) issue(nbm, nbn, 0, 1);
-  load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0));
+  load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0), f1);
   int st = 0;
   for (;;) {
     for (int kt = 0; kt < nk; ++kt) {
@@ -505,15 +507,15 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       // sched_barrier keeps each phase where it is written: without it the
       // scheduler hoists every quarter's reads to the top and runs out of VGPRs
       const int vb = blocks_in(kt);
-      load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane, vb);
+      load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 0>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
-      load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane, vb);
+      load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane, vb, f1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 2>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
-      load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane, vb);
+      load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 0>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
@@ -527,7 +529,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
         if (kt + 2 < nk) issue(bm, bn, kt + 2, st);
         else if (rn < w.rounds && kt + 2 - nk < nk) issue(nbm, nbn, kt + 2 - nk, st);
         st ^= 1;
-        load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0));
+        load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0), f1);
       }
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 2>(f1, acc, shift);
