@@ -56,10 +56,14 @@ __device__ __forceinline__ void e1m2_to_e2m3(const uint32_t (&in)[4], uint32_t (
   }
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // quiet NaN
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// Two floats to packed bf16 (a in the low half) by gfx950's packed conversion:
+// round to nearest even, a NaN quieted with its payload kept.  Over all 2^32
+// float inputs it gives the same bits as the plain definition, that is
+// (u + 0x7FFF + bit 16 of u) >> 16 for non-NaN u, and (u >> 16) | 0x40 for NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // Tile order: workgroup ids are dealt round-robin to the 8 XCDs.  Groups of
@@ -162,7 +166,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, int64_t row0, in
           if constexpr (OUT == MX_OUT_F32)
             ((float*)p.c)[row * p.ldc + col] = acc[i][j][r];
           else
-            ((uint16_t*)p.c)[row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+            ((uint16_t*)p.c)[row * p.ldc + col] = (uint16_t)pack_bf16(acc[i][j][r], 0.0f);
         }
       }
     }
@@ -223,8 +227,7 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
           typedef float f4v __attribute__((ext_vector_type(4)));
           __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, (f4v*)((float*)p.c + row * p.ldc + col));
         } else {
-          const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi2 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          const uint32_t lo = pack_bf16(v[0], v[1]), hi2 = pack_bf16(v[2], v[3]);
           typedef unsigned int u2v __attribute__((ext_vector_type(2)));
           __builtin_nontemporal_store(u2v{lo, hi2}, (u2v*)((uint16_t*)p.c + row * p.ldc + col));
         }
