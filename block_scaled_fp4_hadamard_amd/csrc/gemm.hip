@@ -399,7 +399,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   int r = next_round(tm, w, 0, bm, bn);
   if (r >= w.rounds) return;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int r0 = wm * 128, c0 = wn * 64;
   const int nk = (int)((p.K + 255) / 256);
@@ -415,17 +415,21 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   // stalled every SIMD behind the copies.  The
   // wave covers rows 32(w & 3) + 128h .. +31 of A and of B (h = 0, 1), and
   // the scale dwords of rows 64(w & 3) + lane of both.  Offsets are from the
-  // tile's first row (operands are < 4 GiB).
-  uint32_t oa[8], ob[8];
+  // tile's first row (operands are < 4 GiB).  Copy e = 4h + c covers rows
+  // 32(w & 3) + 128h + 8c + lane/8; the slot swizzle of such a row depends on
+  // c only through c & 1, so each lane keeps two offsets per operand and adds
+  // the copy's wave-uniform row base.
+  uint32_t la[2], lb[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int row = 32 * (wave & 3) + 128 * h + 8 * c + (lane >> 3);
-      const int piece = (lane & 7) ^ ((row >> 1) & 7);
-      oa[4 * h + c] = (uint32_t)(row * p.lda_codes + piece * 16);
-      ob[4 * h + c] = (uint32_t)(row * p.ldb_codes + piece * 16);
-    }
+  for (int c = 0; c < 2; ++c) {
+    const int row = 8 * c + (lane >> 3);
+    const int piece = (lane & 7) ^ ((row >> 1) & 7);
+    la[c] = (uint32_t)(row * p.lda_codes + piece * 16);
+    lb[c] = (uint32_t)(row * p.ldb_codes + piece * 16);
+  }
+  auto copy_rows = [&](int e) { return 32 * (wave & 3) + 128 * (e >> 2) + 8 * (e & 2); };
+  auto offa = [&](int e) { return la[e & 1] + (uint32_t)(copy_rows(e) * p.lda_codes); };
+  auto offb = [&](int e) { return lb[e & 1] + (uint32_t)(copy_rows(e) * p.ldb_codes); };
   const int srow = 64 * (wave & 3) + lane;
   const uint32_t osa = (uint32_t)(srow * p.lda_scales), osb = (uint32_t)(srow * p.ldb_scales);
   const uint32_t lA = lds_addr(&sA[0][32 * (wave & 3) * kRowBytes]), lB = lds_addr(&sB[0][32 * (wave & 3) * kRowBytes]);
@@ -446,8 +450,8 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          dma16_off(abase, oa[4 * h + c] + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
-          dma16_off(bbase, ob[4 * h + c] + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+          dma16_off(abase, offa(4 * h + c) + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+          dma16_off(bbase, offb(4 * h + c) + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
         }
       dma4_off(sabase, osa + 8 * kt, lSA + st * (2 * kBM * 4));
       dma4_off(sabase, osa + 8 * kt + 4, lSA + st * (2 * kBM * 4) + kBM * 4);
@@ -465,8 +469,8 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
           const int gp = (lane & 7) ^ (4 * (c & 1) + (lane >> 4));
           const int rowoff = (32 * (wave & 3) + 128 * h + 8 * c) * kRowBytes + 16 * lane;
           if (gp < vb) {
-            dma16_off(abase, oa[4 * h + c] + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
-            dma16_off(bbase, ob[4 * h + c] + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+            dma16_off(abase, offa(4 * h + c) + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+            dma16_off(bbase, offb(4 * h + c) + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
           } else {
             *(uint4*)(&sA[st][rowoff]) = uint4{0u, 0u, 0u, 0u};
             *(uint4*)(&sB[st][rowoff]) = uint4{0u, 0u, 0u, 0u};
