@@ -103,13 +103,15 @@ __device__ __forceinline__ void load_group(const uint16_t* xr, int64_t cols, int
 }
 
 // tree sum of m^p over the 128 blocks of a group: within each chunk by a lane
-// butterfly (quads 1, 2, 4, 8 apart), then over the 8 chunks in registers
+// butterfly (quads 1, 2, 4, 8 apart), then over the 8 chunks in registers.
+// bmax: each chunk's block absmax as bf16 magnitude bits (NaN kept)
 template <int P>
-__device__ __forceinline__ double group_sum(const uint4 (&v)[kGroupChunks]) {
+__device__ __forceinline__ double group_sum(const uint4 (&v)[kGroupChunks], uint32_t (&bmax)[kGroupChunks]) {
   double s[kGroupChunks];
 #pragma unroll
   for (int ch = 0; ch < kGroupChunks; ++ch) {
     uint32_t mb = quad_max(max_mag8(v[ch]));
+    bmax[ch] = mb;
     if (mb > 0x7F80u) mb = 0x7F80u;                           // NaN counts as +inf
     const double m = (double)__uint_as_float(mb << 16);
     s[ch] = P == 1 ? m : m * m;                               // exact
@@ -122,20 +124,20 @@ __device__ __forceinline__ double group_sum(const uint4 (&v)[kGroupChunks]) {
 }
 
 // cast 8 values of one lane (a quarter of block col / 32) into a code word;
-// returns the block's scale byte
+// returns the block's scale byte.  xmax: the block's absmax as bf16 magnitude
+// bits.  Since rho >= 0 and rounding is monotonic and odd, the block's
+// max |y| = max RN32(|x| rho) is RN32(max |x| * rho), NaN and inf included.
 template <int GRID, int ROUND>
-__device__ __forceinline__ uint32_t cast8(const uint4& v, float rho, int64_t elem, uint32_t k0, uint32_t k1,
-                                          uint32_t& word) {
+__device__ __forceinline__ uint32_t cast8(const uint4& v, uint32_t xmax, float rho, int64_t elem, uint32_t k0,
+                                          uint32_t k1, uint32_t& word) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float y[8];
-  uint32_t mb = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     y[2 * i] = __uint_as_float(w[i] << 16) * rho;
     y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u) * rho;
-    mb = max(mb, max(__float_as_uint(y[2 * i]) & 0x7FFFFFFFu, __float_as_uint(y[2 * i + 1]) & 0x7FFFFFFFu));
   }
-  mb = quad_max(mb);
+  const uint32_t mb = __float_as_uint(__uint_as_float(xmax << 16) * rho) & 0x7FFFFFFFu;
   const bool nonfinite = mb >= 0x7F800000u;
   const uint32_t byte = nonfinite ? 0xFFu : scale_byte<GRID>(mb >> 23);
   uint32_t r = 0;
@@ -177,14 +179,16 @@ __global__ void __launch_bounds__(64 * kNormWaves) mxnorm_kernel(const MxNormPar
   // ---- pass 1: block maxima, m^p, the tree sum (groups of 8 chunks; the
   // group sums meet in a 16-slot butterfly)
   uint4 v[kGroupChunks];
+  uint32_t bmax[kGroupChunks];
   load_group(xr, p.cols, 0, lane, v);
-  double total = group_sum<P>(v);
+  double total = group_sum<P>(v, bmax);
   if (ngroups > 1) {
     if (lane == 0) group_sums[wave][0] = total;
     for (int g = 1; g < ngroups; ++g) {
       uint4 w[kGroupChunks];
+      uint32_t wmax[kGroupChunks];
       load_group(xr, p.cols, g, lane, w);
-      const double gs = group_sum<P>(w);
+      const double gs = group_sum<P>(w, wmax);
       if (lane == 0) group_sums[wave][g] = gs;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0): the sums are in LDS
@@ -203,16 +207,23 @@ __global__ void __launch_bounds__(64 * kNormWaves) mxnorm_kernel(const MxNormPar
   // ---- pass 2: y = RN32(x * rho), block scale, cast, pack (the first
   // group is still in registers)
   const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
+  uint32_t* const crow = (uint32_t*)(p.codes + row * p.ld_codes) + lane;    // 4 code bytes per lane and chunk
+  uint8_t* const srow = p.scales + row * p.ld_scales + lane / 4;
   for (int g = 0; g < ngroups; ++g) {
-    if (g > 0) load_group(xr, p.cols, g, lane, v);
+    if (g > 0) {
+      load_group(xr, p.cols, g, lane, v);
+#pragma unroll
+      for (int ch = 0; ch < kGroupChunks; ++ch) bmax[ch] = quad_max(max_mag8(v[ch]));
+    }
 #pragma unroll
     for (int ch = 0; ch < kGroupChunks; ++ch) {
       const int64_t col = ((int64_t)g * kGroupChunks + ch) * kChunk + 8 * lane;
       uint32_t word;
-      const uint32_t byte = cast8<GRID, ROUND>(v[ch], rho, row * p.cols + col, k0, k1, word);
+      const uint32_t byte = cast8<GRID, ROUND>(v[ch], bmax[ch], rho, row * p.cols + col, k0, k1, word);
       if (col < p.cols) {
-        __builtin_nontemporal_store(word, (uint32_t*)(p.codes + row * p.ld_codes + col / 2));   // written once
-        if ((lane & 3) == 0) p.scales[row * p.ld_scales + col / 32] = (uint8_t)byte;
+        const int c = g * kGroupChunks + ch;
+        __builtin_nontemporal_store(word, crow + 64 * c);                       // written once
+        if ((lane & 3) == 0) srow[16 * c] = (uint8_t)byte;
       }
     }
   }
