@@ -208,30 +208,81 @@ __device__ __forceinline__ void transpose4(float (&v)[4], int lane) {
   }
 }
 
+__device__ __forceinline__ const uint8_t* wave_uniform(const uint8_t* p);
+__device__ __forceinline__ uint32_t dpp_xor1_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_xor2_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+}
+
 template <int OUT, int MT, int NT>
 __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row0, int64_t col0, int lane,
-                                                const v16f (&acc)[MT][NT]) {
+                                                const v16f (&acc)[MT][NT], bool wide16) {
   const int half = lane >> 5, quad = (lane & 31) >> 2, k = lane & 3;
+  if (OUT == MX_OUT_F32 || !wide16) {
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        transpose4(v, lane);
-        const int64_t row = row0 + i * 32 + 8 * g + 4 * half + k;
-        const int64_t col = col0 + j * 32 + 4 * quad;
-        // non-temporal: the output streams past the L2, which keeps the operand panels the next tiles read
-        if constexpr (OUT == MX_OUT_F32) {
-          typedef float f4v __attribute__((ext_vector_type(4)));
-          __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, (f4v*)((float*)p.c + row * p.ldc + col));
-        } else {
-          const uint32_t lo = pack_bf16(v[0], v[1]), hi2 = pack_bf16(v[2], v[3]);
-          typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-          __builtin_nontemporal_store(u2v{lo, hi2}, (u2v*)((uint16_t*)p.c + row * p.ldc + col));
+        for (int g = 0; g < 4; ++g) {
+          float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          transpose4(v, lane);
+          const int64_t row = row0 + i * 32 + 8 * g + 4 * half + k;
+          const int64_t col = col0 + j * 32 + 4 * quad;
+          // non-temporal: the output streams past the L2, which keeps the operand panels the next tiles read
+          if constexpr (OUT == MX_OUT_F32) {
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(f4v{v[0], v[1], v[2], v[3]}, (f4v*)((float*)p.c + row * p.ldc + col));
+          } else {
+            typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u2v{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])},
+                                        (u2v*)((uint16_t*)p.c + row * p.ldc + col));
+          }
         }
-      }
+  } else {
+    // bf16, 16 bytes per lane.  Each 4x4 block is rounded first (P0 = rows 0-1, P1 = rows 2-3 of the
+    // lane's column) and transposed as 16-bit values.  Exchange 1 (lanes l ^ 2): lanes k < 2 keep
+    // rows 0-1 of their own column and get rows 0-1 of column k + 2; lanes k >= 2 keep rows 2-3 and
+    // get those of column k - 2, so that A holds column k & 1 and B column (k & 1) + 2, both for rows
+    // (k & 2) .. +1.  Exchange 2 (lanes l ^ 1) swaps 16-bit halves: an even lane sends the high
+    // halves of A and B, an odd lane the low ones; byte permutes give lane k row k, columns 0-3.
+    // Then the quads of a pair (lanes l ^ 4) trade four columns: for register groups g, g + 1 the even
+    // quad ends with row 8g + 4h + k and the odd quad with row 8g + 8 + 4h + k, each with the pair's
+    // eight columns.  Values are moved, never combined.
+    const bool low = k < 2, odd = (k & 1) != 0, qodd = (quad & 1) != 0;
+    const uint32_t sel_s = odd ? 0x05040100u : 0x07060302u;    // (A, B) -> what goes to the partner
+    const uint32_t sel_q0 = odd ? 0x03020504u : 0x05040100u;   // (R, A) -> columns 0-1
+    const uint32_t sel_q1 = odd ? 0x03020706u : 0x07060100u;   // (R, B) -> columns 2-3
+    // the lane's byte offset from its group pair's first element; the pair's base is wave-uniform
+    const uint32_t loff = (uint32_t)((((4 * half + k) + 8 * (quad & 1)) * p.ldc + 4 * (quad & ~1)) * 2);
+    auto rows4 = [&](const v16f& a4, int g, uint32_t& q0, uint32_t& q1) {
+      const uint32_t p0 = pack_bf16(a4[4 * g], a4[4 * g + 1]), p1 = pack_bf16(a4[4 * g + 2], a4[4 * g + 3]);
+      const uint32_t recv = dpp_xor2_u(low ? p1 : p0);
+      const uint32_t a = low ? p0 : recv, b = low ? recv : p1;
+      const uint32_t r = dpp_xor1_u(__builtin_amdgcn_perm(b, a, sel_s));
+      q0 = __builtin_amdgcn_perm(r, a, sel_q0);
+      q1 = __builtin_amdgcn_perm(r, b, sel_q1);
+    };
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; g += 2) {
+          uint32_t a0, a1, b0, b1;
+          rows4(acc[i][j], g, a0, a1);
+          rows4(acc[i][j], g + 1, b0, b1);
+          // lanes l ^ 4 (bit mode: and 0x1F, xor 4)
+          const uint32_t r0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(qodd ? a0 : b0), 0x101F);
+          const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(qodd ? a1 : b1), 0x101F);
+          typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+          const u4v d = qodd ? u4v{r0, r1, b0, b1} : u4v{a0, a1, r0, r1};
+          const uint8_t* base = wave_uniform((const uint8_t*)p.c + ((row0 + i * 32 + 8 * g) * p.ldc + col0 + j * 32) * 2);
+          __builtin_nontemporal_store(d, (__attribute__((address_space(1))) u4v*)(base + loff));
+        }
+  }
 }
 
 // Global -> LDS DMA of 16 (or 4) bytes per lane: LDS address = M0 + size*lane.
@@ -385,7 +436,7 @@ __device__ __forceinline__ int next_round(const TileMap& tm, const Walk& w, int 
 // that the whole-step kernel carries none of its register cost
 template <int GRID, int OUT, bool RK>
 __global__ void __launch_bounds__(kFullThreads, 1)
-gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
+gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kFullStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kFullStageBytes];
   __shared__ __attribute__((aligned(1024))) uint32_t sSA[2][2 * kBM];    // [dword d][row]: blocks 4d..4d+3
@@ -542,7 +593,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       mfma_quarter<GRID, 2>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile_wide<OUT, 4, 2>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc);
+    store_tile_wide<OUT, 4, 2>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc, wide16);
     if (rn >= w.rounds) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -623,8 +674,10 @@ static void launch_kind(const GemmParams& p, const TileMap& tm, bool full, dim3 
     // one workgroup per CU: 8 XCDs x 32 members; round r deals group r*8+xcd
     const int rounds = (tm.groups + kXcds - 1) / kXcds;
     const dim3 g(kXcds * kGroupM * kGroupN), b(kFullThreads);
-    if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false>), g, b, 0, s, p, tm, rounds);
-    else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true>), g, b, 0, s, p, tm, rounds);
+    // bf16 rows written 16 bytes per lane need 16-byte aligned rows and tile origins
+    const bool wide16 = p.ldc % 8 == 0 && p.N % 8 == 0 && (uintptr_t)p.c % 16 == 0;
+    if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false>), g, b, 0, s, p, tm, rounds, wide16);
+    else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true>), g, b, 0, s, p, tm, rounds, wide16);
   } else {
     hipLaunchKernelGGL((gemm_general_kernel<GRID, OUT>), g, dim3(kGemmThreads), 0, s, p, tm);
   }

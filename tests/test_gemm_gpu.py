@@ -87,6 +87,30 @@ def test_whole_tile_path_ragged_edges(grid, m, n, k):
     assert np.array_equal(c16, want)
 
 
+@pytest.mark.parametrize("pitch,offset", [(512, 0), (516, 0), (520, 0), (1032, 0), (520, 4), (520, 8)])
+def test_bf16_output_row_pitch(pitch, offset):
+    """bf16 output through a strided window: rows whose pitch is a multiple of 8 elements, starting 16-byte
+    aligned, are written 16 bytes per lane, the others 8 bytes per lane.  Each form carries the RNE cast of
+    the fp32 result bit for bit, and nothing outside the M x N window changes."""
+    announce("gemm bf16 output pitch %d offset %d" % (pitch, offset))
+    rng = np.random.default_rng(pitch + offset)
+    m, n, k = 512, 512, 768
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c32 = run_gemm(a, b, "e2m1", torch.float32)
+    qa = QTensor(torch.from_numpy(a[0]).cuda(), torch.from_numpy(a[1]).cuda(), "e2m1")
+    qb = QTensor(torch.from_numpy(b[0]).cuda(), torch.from_numpy(b[1]).cuda(), "e2m1")
+    buf = torch.full((m, pitch + offset), -7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[:, offset:offset + n]
+    assert out.stride(0) == pitch + offset
+    gemm(qa, qb, out=out)
+    torch.cuda.synchronize()
+    host = buf.float().cpu().numpy()
+    want = torch.from_numpy(c32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(host[:, offset:offset + n], want)
+    assert np.all(host[:, :offset] == -7.0) and np.all(host[:, offset + n:] == -7.0)
+
+
 def padded_qtensor(op, grid, fill=0xFF):
     """A GPU operand whose scale rows are padded to a multiple of 4 bytes, the padding set to `fill` (0xFF is
     the NaN scale: any use of it would poison the products)."""
