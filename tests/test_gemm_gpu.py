@@ -87,7 +87,7 @@ def test_whole_tile_path_ragged_edges(grid, m, n, k):
     assert np.array_equal(c16, want)
 
 
-@pytest.mark.parametrize("pitch,offset", [(512, 0), (516, 0), (520, 0), (1032, 0), (520, 4), (520, 8)])
+@pytest.mark.parametrize("pitch,offset", [(512, 0), (516, 0), (520, 0), (1032, 0), (520, 4), (520, 8), (524, 4)])
 def test_bf16_output_row_pitch(pitch, offset):
     """bf16 output through a strided window: rows whose pitch is a multiple of 8 elements, starting 16-byte
     aligned, are written 16 bytes per lane, the others 8 bytes per lane.  Each form carries the RNE cast of
@@ -100,7 +100,7 @@ def test_bf16_output_row_pitch(pitch, offset):
     c32 = run_gemm(a, b, "e2m1", torch.float32)
     qa = QTensor(torch.from_numpy(a[0]).cuda(), torch.from_numpy(a[1]).cuda(), "e2m1")
     qb = QTensor(torch.from_numpy(b[0]).cuda(), torch.from_numpy(b[1]).cuda(), "e2m1")
-    buf = torch.full((m, pitch + offset), -7.0, dtype=torch.bfloat16, device="cuda")
+    buf = torch.full((m, pitch + offset), -7.0, dtype=torch.bfloat16, device="cuda")   # row pitch: pitch + offset
     out = buf[:, offset:offset + n]
     assert out.stride(0) == pitch + offset
     gemm(qa, qb, out=out)
