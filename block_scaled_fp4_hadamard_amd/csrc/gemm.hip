@@ -176,10 +176,12 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, int64_t row0, in
 // registers (four consecutive rows) and each quad of lanes (four consecutive
 // columns) the 4x4 block is transposed with two DPP exchanges (lane pairs
 // l ^ 1, then l ^ 2), after which lane 4a + k holds row k of the block,
-// columns 4a .. 4a + 3 in order: one 16-byte (fp32) or 8-byte (bf16) store
-// per lane and register group, every row segment a whole 128- or 64-byte
-// run.  Values are moved, never combined, so the stored numbers are the
-// accumulators' bit for bit.
+// columns 4a .. 4a + 3 in order: one 16-byte fp32 store per lane and register
+// group, every row segment a whole 128-byte run.  bf16 goes further (below):
+// neighbouring quads pair up so that each lane stores eight columns, 16
+// bytes, since the store instruction count bounds the epilogue.  Values are
+// moved, never combined, so the stored numbers are the accumulators' (or
+// their bf16 roundings) bit for bit.
 __device__ __forceinline__ float dpp_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
 }
