@@ -177,7 +177,7 @@ def measure_block16(tensors, dev, reps=30):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: there is no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         return 2
     if args.calibrate_copy:
