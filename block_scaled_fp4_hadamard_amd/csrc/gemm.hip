@@ -250,15 +250,15 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
     // get those of column k - 2, so that A holds column k & 1 and B column (k & 1) + 2, both for rows
     // (k & 2) .. +1.  Exchange 2 (lanes l ^ 1) swaps 16-bit halves: an even lane sends the high
     // halves of A and B, an odd lane the low ones; byte permutes give lane k row k, columns 0-3.
-    // Then the quads of a pair (lanes l ^ 4) trade four columns: for register groups g, g + 1 the even
-    // quad ends with row 8g + 4h + k and the odd quad with row 8g + 8 + 4h + k, each with the pair's
-    // eight columns.  Values are moved, never combined.
+    // Then the quads of a pair (lanes l ^ 4) trade four columns: the even quad ends with eight columns
+    // of the wave's left 32-column half, the odd quad with eight of the right half, for the same row.
+    // One store then writes eight whole 128-byte rows.  Values are moved, never combined.
     const bool low = k < 2, odd = (k & 1) != 0, qodd = (quad & 1) != 0;
     const uint32_t sel_s = odd ? 0x05040100u : 0x07060302u;    // (A, B) -> what goes to the partner
     const uint32_t sel_q0 = odd ? 0x03020504u : 0x05040100u;   // (R, A) -> columns 0-1
     const uint32_t sel_q1 = odd ? 0x03020706u : 0x07060100u;   // (R, B) -> columns 2-3
-    // the lane's byte offset from its group pair's first element; the pair's base is wave-uniform
-    const uint32_t loff = (uint32_t)((((4 * half + k) + 8 * (quad & 1)) * p.ldc + 4 * (quad & ~1)) * 2);
+    // the lane's byte offset from its row group's first element; the group's base is wave-uniform
+    const uint32_t loff = (uint32_t)(((4 * half + k) * p.ldc + 4 * (quad & ~1) + 32 * (quad & 1)) * 2);
     auto rows4 = [&](const v16f& a4, int g, uint32_t& q0, uint32_t& q1) {
       const uint32_t p0 = pack_bf16(a4[4 * g], a4[4 * g + 1]), p1 = pack_bf16(a4[4 * g + 2], a4[4 * g + 3]);
       const uint32_t recv = dpp_xor2_u(low ? p1 : p0);
@@ -267,23 +267,32 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
       q0 = __builtin_amdgcn_perm(r, a, sel_q0);
       q1 = __builtin_amdgcn_perm(r, b, sel_q1);
     };
+    static_assert(NT == 2, "a row of the wave's tile is two 32-column halves");
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int g = 0; g < 4; g += 2) {
+        // rows R = 8g + 4h + k and R + 8, each in the left (j = 0) and right (j = 1) half
+        uint32_t a0[2], a1[2], b0[2], b1[2];
+        rows4(acc[i][0], g, a0[0], a0[1]);
+        rows4(acc[i][1], g, a1[0], a1[1]);
+        rows4(acc[i][0], g + 1, b0[0], b0[1]);
+        rows4(acc[i][1], g + 1, b1[0], b1[1]);
+        // an even quad keeps the left half and gets its partner's left columns; an odd quad keeps the
+        // right half (lanes l ^ 4; bit mode: and 0x1F, xor 4)
+        uint32_t ra[2], rb[2];
 #pragma unroll
-        for (int g = 0; g < 4; g += 2) {
-          uint32_t a0, a1, b0, b1;
-          rows4(acc[i][j], g, a0, a1);
-          rows4(acc[i][j], g + 1, b0, b1);
-          // lanes l ^ 4 (bit mode: and 0x1F, xor 4)
-          const uint32_t r0 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(qodd ? a0 : b0), 0x101F);
-          const uint32_t r1 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(qodd ? a1 : b1), 0x101F);
-          typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-          const u4v d = qodd ? u4v{r0, r1, b0, b1} : u4v{a0, a1, r0, r1};
-          const uint8_t* base = wave_uniform((const uint8_t*)p.c + ((row0 + i * 32 + 8 * g) * p.ldc + col0 + j * 32) * 2);
-          __builtin_nontemporal_store(d, (__attribute__((address_space(1))) u4v*)(base + loff));
+        for (int d = 0; d < 2; ++d) {
+          ra[d] = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(qodd ? a0[d] : a1[d]), 0x101F);
+          rb[d] = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(qodd ? b0[d] : b1[d]), 0x101F);
         }
+        typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+        const u4v da = qodd ? u4v{ra[0], ra[1], a1[0], a1[1]} : u4v{a0[0], a0[1], ra[0], ra[1]};
+        const u4v db = qodd ? u4v{rb[0], rb[1], b1[0], b1[1]} : u4v{b0[0], b0[1], rb[0], rb[1]};
+        const uint8_t* base = wave_uniform((const uint8_t*)p.c + ((row0 + i * 32 + 8 * g) * p.ldc + col0) * 2);
+        __builtin_nontemporal_store(da, (__attribute__((address_space(1))) u4v*)(base + loff));
+        __builtin_nontemporal_store(db, (__attribute__((address_space(1))) u4v*)(base + loff + 16 * p.ldc));
+      }
   }
 }
 
