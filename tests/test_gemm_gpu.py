@@ -111,6 +111,28 @@ def test_bf16_output_row_pitch(pitch, offset):
     assert np.all(host[:, :offset] == -7.0) and np.all(host[:, offset + n:] == -7.0)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+def test_fast_and_general_kernels_agree_bitwise(out_dtype, grid):
+    """The same operands through the whole-tile kernel (aligned output) and through the bounds-checked
+    kernel (an output window one element off alignment): both sum K in 64-deep MFMA steps in order, so the
+    outputs carry the same bits."""
+    announce("gemm fast vs general %s %s" % (grid, out_dtype))
+    rng = np.random.default_rng(77)
+    m, n, k = 512, 512, 1024
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    qa = QTensor(torch.from_numpy(a[0]).cuda(), torch.from_numpy(a[1]).cuda(), grid)
+    qb = QTensor(torch.from_numpy(b[0]).cuda(), torch.from_numpy(b[1]).cuda(), grid)
+    fast = gemm(qa, qb, out_dtype=out_dtype)
+    buf = torch.zeros((m, n + 4), dtype=out_dtype, device="cuda")
+    general = buf[:, 1:1 + n]
+    gemm(qa, qb, out=general)
+    torch.cuda.synchronize()
+    iv = torch.int32 if out_dtype == torch.float32 else torch.int16
+    assert torch.equal(fast.view(iv).cpu(), general.contiguous().view(iv).cpu())
+
+
 def padded_qtensor(op, grid, fill=0xFF):
     """A GPU operand whose scale rows are padded to a multiple of 4 bytes, the padding set to `fill` (0xFF is
     the NaN scale: any use of it would poison the products)."""
