@@ -96,7 +96,9 @@ class LlamaBlockStep:
             if len(parts) > 1:
                 self.operands["w_" + name] = torch.cat([t["w_" + p] for p in parts], dim=0).contiguous()
                 self.operands["dy_" + name] = torch.cat([t["dy_" + p] for p in parts], dim=1).contiguous()
-        # quantize every input once (both axes), each weight, each gradient
+        # quantize every input once (both axes), each weight, each gradient; the SR seeds follow the
+        # tensors' sorted order, whatever the launch order
+        quant = {}
         for ordinal, name in enumerate(tensor_names(r.fuse)):
             x = self.operands[name]
             rows, cols = x.shape
@@ -109,8 +111,15 @@ class LlamaBlockStep:
             fn = (lambda x=x, qrow=qrow, qcol=qcol, rounding=rounding, seed=seed:
                   api.quantize(x, axis="both", grid=r.grid, rounding=rounding, seed=seed, had_n=r.had_n,
                                had_kind=r.had_kind, had_seed=r.had_seed, row_out=qrow, col_out=qcol))
-            self.launches.append(Launch("quant." + rounding, "quantize " + name, fn, quant_bytes(rows, cols)))
+            quant[name] = Launch("quant." + rounding, "quantize " + name, fn, quant_bytes(rows, cols))
+        # each projection's quantizations run just before its three GEMMs, as in a training step: the
+        # quantized operands are then still in the last-level cache when the GEMMs read them
+        done = set()
         for name, parts in proj.items():
+            for tname in (LLAMA_INPUT_OF[parts[0]], "w_" + name, "dy_" + name):
+                if tname not in done:
+                    self.launches.append(quant[tname])
+                    done.add(tname)
             o = sum(LLAMA_LINEARS[p][0] for p in parts)
             i = LLAMA_LINEARS[parts[0]][1]
             xq, wq, dq = self.q[LLAMA_INPUT_OF[parts[0]]], self.q["w_" + name], self.q["dy_" + name]
