@@ -473,10 +473,12 @@ constexpr int kWaitLgkm0 = 0xC07F;
 
 // global -> LDS copy of 16 bytes per lane (gfx950 LDS DMA): lane l's bytes
 // land at LDS address m0 + 16 l.  The s_nop covers the M0 write hazard.  The
-// input is read once, so the copy is non-temporal; so are the row-wise
-// outputs, whole lines written once.  The column-wise outputs are not: their
-// 16-byte pieces of a line meet in L2, and streaming them past it made the
-// kernel 1.6x slower.
+// input is read once, so the copy is non-temporal.  The outputs are plain
+// stores: the GEMMs that consume them often run next and then find them in
+// the last-level cache (streaming the row-wise outputs past it saved a few
+// percent here but cost the step more), and the column-wise outputs' 16-byte
+// pieces of a line must meet in L2 (streaming them made the kernel 1.6x
+// slower).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
@@ -558,7 +560,7 @@ __device__ __forceinline__ void store_row_scales(uint8_t* dst, int k, uint32_t b
   if (!active) return;
   if (wide) {
     typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-    if (k == 0) __builtin_nontemporal_store(u2v{v, hi}, (u2v*)dst);
+    if (k == 0) *(u2v*)dst = u2v{v, hi};
   } else {
     dst[k] = (uint8_t)byte;
   }
@@ -692,7 +694,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       // counter of the lane's first output: (row * cols + c0) / 4 + 4 hl, and cols % 8 == 0
       const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)p.cols, 0u, k0, k1, w);
       typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-      if (valid) __builtin_nontemporal_store(u2v{w[0], w[1]}, (u2v*)(cbase + 4 * g * p.ld_row_codes));
+      if (valid) *(u2v*)(cbase + 4 * g * p.ld_row_codes) = u2v{w[0], w[1]};
       store_row_scales(sbase + 4 * g * p.ld_row_scales, k, byte, wide_scales && full_width, valid && hl == 0);
     }
   }
