@@ -115,19 +115,21 @@ def measure_mxnorm(tensors, dev, reps=30):
     """
     import torch
     from block_scaled_fp4_hadamard_amd import mxnorm_quantize
+    from block_scaled_fp4_hadamard_amd.mxnorm_constant import correction
+    c = correction(2)
     names = ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"]
     xs = [tensors[n] for n in names]
     rows, cols = xs[0].shape
-    outs = [mxnorm_quantize(x, power=2) for x in xs]
+    outs = [mxnorm_quantize(x, power=2, c=c) for x in xs]
     for i, x in enumerate(xs):
-        mxnorm_quantize(x, power=2, out=outs[i][0], rho=outs[i][1])
+        mxnorm_quantize(x, power=2, c=c, out=outs[i][0], rho=outs[i][1])
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for j in range(reps):
         i = j % len(xs)
-        mxnorm_quantize(xs[i], power=2, out=outs[i][0], rho=outs[i][1])
+        mxnorm_quantize(xs[i], power=2, c=c, out=outs[i][0], rho=outs[i][1])
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3

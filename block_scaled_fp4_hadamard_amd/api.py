@@ -3,9 +3,7 @@ the tensor's device and launch on torch's current stream.  No arithmetic of
 the method happens here.
 """
 from dataclasses import dataclass
-from functools import lru_cache
 
-import numpy as np
 import torch
 
 from . import _lib
@@ -16,11 +14,12 @@ class QTensor:
     """A block-scaled 4-bit operand: L lines of length K, K-contiguous.
 
     codes  uint8 (L, K/2): element 2j of a line in the low nibble of byte j
-    scales uint8 (L, K/32): E8M0 exponent byte per 32-element block
+    scales uint8 (L, K/block): E8M0 exponent byte per block of `block` (32, or 16) elements
     """
     codes: torch.Tensor
     scales: torch.Tensor
     grid: str = "e2m1"
+    block: int = 32           # values per E8M0 scale: scales hold K / block bytes per line
 
     @property
     def lines(self):
@@ -36,6 +35,8 @@ class QTensor:
 
 
 def _stream(dev):
+    if dev.type != "cuda":
+        return None       # host tensors reach only the library's argument checks, which launch nothing
     return ctypes_void(torch.cuda.current_stream(dev).cuda_stream)
 
 
@@ -56,7 +57,7 @@ def empty_qtensor(lines, k, device, grid="e2m1", block=32):
     (the padding is never read as data)."""
     nb = k // block
     scales = torch.empty((lines, (nb + 3) // 4 * 4), dtype=torch.uint8, device=device)[:, :nb]
-    return QTensor(torch.empty((lines, k // 2), dtype=torch.uint8, device=device), scales, grid)
+    return QTensor(torch.empty((lines, k // 2), dtype=torch.uint8, device=device), scales, grid, block)
 
 
 def quantize(x, axis="row", grid="e2m1", rounding="rtne", seed=0, had_n=0, had_kind="det", had_seed=0,
@@ -71,6 +72,9 @@ def quantize(x, axis="row", grid="e2m1", rounding="rtne", seed=0, had_n=0, had_k
     rows, cols = x.shape
     dev = x.device
     do_row, do_col = axis in ("row", "both"), axis in ("col", "both")
+    for given in (row_out, col_out):
+        if given is not None and given.block != block:
+            raise ValueError("an output operand of block %d given for block %d" % (given.block, block))
     out = {}
     rq = cq = None
     if do_row:
@@ -93,52 +97,42 @@ def quantize(x, axis="row", grid="e2m1", rounding="rtne", seed=0, had_n=0, had_k
 
 
 def gemm(a, b, out_dtype=torch.float32, out=None, grid=None):
-    """C = A B^T on the decoded operands (M x N), fp32 accumulation, fp32 or bf16 output."""
+    """C = A B^T on the decoded operands (M x N), fp32 accumulation, fp32 or bf16 output.
+
+    The operands' block size goes to the library as it is (a 16-value operand is refused there: the matrix
+    cores take 32-value blocks).
+    """
     if a.k != b.k:
         raise ValueError("operands disagree on K: %d vs %d" % (a.k, b.k))
+    if a.block != b.block:
+        raise ValueError("operands disagree on the block size: %d vs %d" % (a.block, b.block))
+    for name, q in (("a", a), ("b", b)):
+        if q.scales.shape[1] * q.block != q.k:
+            raise ValueError("%s: %d scale bytes per line do not cover K = %d in blocks of %d"
+                             % (name, q.scales.shape[1], q.k, q.block))
     grid = grid or a.grid
     M, N, K = a.lines, b.lines, a.k
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
     kind = {torch.float32: "f32", torch.bfloat16: "bf16"}[out.dtype]
-    st = _lib.mx_gemm(a.c_struct(), b.c_struct(), M, N, K, _lib.GRID[grid], 32, out.data_ptr(), out.stride(0),
+    st = _lib.mx_gemm(a.c_struct(), b.c_struct(), M, N, K, _lib.GRID[grid], a.block, out.data_ptr(), out.stride(0),
                       _lib.OUT[kind], _stream(out.device))
     _lib.check(st, "mx_gemm")
     return out
 
 
-@lru_cache(maxsize=None)
-def mxnorm_correction(power=2, block=32, samples=1 << 21, seed=20260121):
-    """The correction constant c(p, B) of the MXNorm estimate, by Monte Carlo.
-
-    "MXNorm: Reusing MXFP block scales ...", Sommario tecnico 2: the constant that
-    makes c * (mean of m^p)^(-1/p) the inverse RMS of rows of i.i.d. values; for
-    standard normal values it is E[M^p]^(1/p) with M the largest |value| of a
-    block.  Estimated from `samples` seeded blocks on the host (relative error
-    about 1e-3 at the default size), returned as a float32 value.
-    """
-    rng = np.random.default_rng(seed)
-    acc, done = 0.0, 0
-    while done < samples:
-        n = min(1 << 16, samples - done)
-        m = np.abs(rng.standard_normal((n, block))).max(axis=1)
-        acc += float(np.sum(m ** power))
-        done += n
-    return float(np.float32((acc / samples) ** (1.0 / power)))
-
-
-def mxnorm_quantize(x, power=2, c=None, grid="e2m1", rounding="rtne", seed=0, out=None, rho=None):
+def mxnorm_quantize(x, power, c, grid="e2m1", rounding="rtne", seed=0, out=None, rho=None):
     """MXNorm of every row of a 2-D bf16 CUDA tensor fused with its row-wise MX cast.
 
-    Returns (QTensor of the normalized rows, rho float32 (rows,)).  c defaults to
-    mxnorm_correction(power).
+    Returns (QTensor of the normalized rows, rho float32 (rows,)).  c is the caller's correction constant
+    c(power, 32) (precomputed once on the host, e.g. by mxnorm_constant.correction).
     """
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     xb = _bits_view(x)
     rows, cols = x.shape
     dev = x.device
-    c = mxnorm_correction(power) if c is None else float(c)
+    c = float(c)
     q = out if out is not None else empty_qtensor(rows, cols, dev, grid)
     r = rho if rho is not None else torch.empty((rows,), dtype=torch.float32, device=dev)
     st = _lib.mx_mxnorm_quantize(xb.data_ptr(), rows, cols, xb.stride(0), power, c, _lib.GRID[grid],
@@ -148,8 +142,9 @@ def mxnorm_quantize(x, power=2, c=None, grid="e2m1", rounding="rtne", seed=0, ou
 
 
 def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0, stats=None):
-    """Diagnostics of one quantized output q of x: SQNR (dB), noise and signal energy, magnitude-code counts,
-    effective bucket ratio (exp(entropy) / 8).  stats: an optional zeroed float64 (12,) CUDA tensor to reuse.
+    """Diagnostic totals of one quantized output q of x, as the kernel accumulates them: sum of y^2, sum of
+    (y - y_hat)^2, the counts of the 8 magnitude codes and the number of blocks.  stats: an optional zeroed
+    float64 (12,) CUDA tensor to reuse.  Ratios built from these (SQNR, bucket usage) are the caller's.
     """
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
@@ -162,14 +157,9 @@ def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0
                              buf.data_ptr(), _stream(x.device))
     _lib.check(st, "mx_quant_stats")
     host = buf.cpu()
-    sums = host[:2].numpy()
-    counts = host[2:].view(torch.int64).numpy()
-    hist, blocks = counts[:8].copy(), int(counts[8])
-    p = hist[hist > 0] / max(hist.sum(), 1)
-    ratio = float(np.exp(-np.sum(p * np.log(p))) / 8.0) if p.size else 0.0
-    sqnr = float("inf") if sums[1] == 0 else float(10.0 * np.log10(sums[0] / sums[1]))
-    return {"sqnr_db": sqnr, "sum_sq": float(sums[0]), "sum_err_sq": float(sums[1]), "hist": hist.tolist(),
-            "blocks": blocks, "bucket_ratio": ratio}
+    counts = host[2:].view(torch.int64)
+    return {"sum_sq": float(host[0]), "sum_err_sq": float(host[1]), "hist": [int(v) for v in counts[:8]],
+            "blocks": int(counts[8])}
 
 
 @dataclass

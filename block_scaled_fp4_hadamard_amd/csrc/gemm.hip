@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "mx_kernels.h"
+#include "gemm_path.h"
 
 namespace mx {
 
@@ -703,15 +704,9 @@ hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStre
   tm.groups = tm.groups_m * groups_n;
   const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
   const dim3 g((unsigned)wgs);
-  // the DMA path needs at least one whole tile along M and N (a ragged last
-  // tile is moved back to end at the edge), at least two 256-element K steps
-  // (a ragged last step is zero-filled), 4-byte aligned scale rows, and
-  // output rows and columns aligned for its 16-byte (fp32) or 8-byte (bf16)
-  // stores
-  const bool full = (p.M >= kBM) && (p.N >= kBN) && (p.N % 4 == 0) && (p.K >= 512) &&
-                    ((uintptr_t)p.a_scales % 4 == 0) && ((uintptr_t)p.b_scales % 4 == 0) &&
-                    (p.lda_scales % 4 == 0) && (p.ldb_scales % 4 == 0) &&
-                    (p.ldc % 4 == 0) && ((uintptr_t)p.c % (out_kind == MX_OUT_F32 ? 16 : 8) == 0);
+  const bool full = gemm_full_path(p.M, p.N, p.K, (uintptr_t)p.a_scales, (uintptr_t)p.b_scales, p.lda_codes,
+                                   p.ldb_codes, p.lda_scales, p.ldb_scales, (uintptr_t)p.c, p.ldc,
+                                   out_kind == MX_OUT_F32);
   if (grid_kind == MX_GRID_E2M1) {
     if (out_kind == MX_OUT_F32) launch_kind<MX_GRID_E2M1, MX_OUT_F32>(p, tm, full, g, s);
     else launch_kind<MX_GRID_E2M1, MX_OUT_BF16>(p, tm, full, g, s);

@@ -9,8 +9,9 @@ quantization over the quantization alone (1.06-1.07x on the pages' hardware).
 
     python -m block_scaled_fp4_hadamard_amd.diagnostics [--tensor activation|gradient|weight]
 
-Every number comes from the HIP kernels (quantizer, mx_quant_stats); this
-module only sequences the calls and prints one JSON line per case.
+The totals come from the HIP kernels (quantizer, mx_quant_stats); this report
+turns them into the two ratios (sqnr_db, bucket_ratio) and prints one JSON
+line per case.
 """
 import argparse
 import json
@@ -34,6 +35,23 @@ def _time_us(fn, reps=20):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def sqnr_db(stats):
+    """Signal-to-quantization-noise ratio in dB from the kernel's totals: 10 log10(sum y^2 / sum (y - y_hat)^2)."""
+    if stats["sum_err_sq"] == 0.0:
+        return float("inf")
+    return float(10.0 * np.log10(stats["sum_sq"] / stats["sum_err_sq"]))
+
+
+def bucket_ratio(stats):
+    """Effective bucket ratio exp(H) / 8, H the entropy of the magnitude-code histogram: the number of the 8
+    codes in effective use, as a fraction of 8 (the pages name the quantity but give no formula)."""
+    hist = np.asarray(stats["hist"], dtype=np.float64)
+    if hist.sum() == 0:
+        return 0.0
+    p = hist[hist > 0] / hist.sum()
+    return float(np.exp(-np.sum(p * np.log(p))) / 8.0)
+
+
 def report(x, axis="row", had_n=32, had_seed=20250, rounding="rtne", seed=0, timing=True):
     """Rows of results for E2M1 and E1M2, without and with the random-sign rotation (and their delta)."""
     out = []
@@ -43,10 +61,10 @@ def report(x, axis="row", had_n=32, had_seed=20250, rounding="rtne", seed=0, tim
             q = api.quantize(x, axis=axis, grid=grid, rounding=rounding, seed=seed, had_n=rot, had_kind="rand",
                              had_seed=had_seed)[axis]
             res[rot] = api.quant_stats(x, q, axis, grid, rot, "rand", had_seed)
+        s0, s1 = sqnr_db(res[0]), sqnr_db(res[had_n])
         row = {"grid": grid, "axis": axis, "rounding": rounding,
-               "sqnr_db": round(res[0]["sqnr_db"], 3), "sqnr_db_rht": round(res[had_n]["sqnr_db"], 3),
-               "delta_sqnr_db": round(res[had_n]["sqnr_db"] - res[0]["sqnr_db"], 3),
-               "bucket_ratio": round(res[0]["bucket_ratio"], 4), "bucket_ratio_rht": round(res[had_n]["bucket_ratio"], 4)}
+               "sqnr_db": round(s0, 3), "sqnr_db_rht": round(s1, 3), "delta_sqnr_db": round(s1 - s0, 3),
+               "bucket_ratio": round(bucket_ratio(res[0]), 4), "bucket_ratio_rht": round(bucket_ratio(res[had_n]), 4)}
         out.append(row)
     if timing:
         t_plain = _time_us(lambda: api.quantize(x, axis="both"))

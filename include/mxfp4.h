@@ -156,9 +156,11 @@ mx_status mx_hadamard_quantize(const uint16_t *x, int64_t rows, int64_t cols, in
  *              of the fp32 result); aligned to its element size, ldc >= N
  * Any accepted shape gives the same numbers.  The fast path (256 x 256 tiles
  * fed by LDS copies) takes M, N >= 256, N % 4 == 0, K >= 512, 4-byte aligned
- * scale rows with ld_scales % 4 == 0, ldc % 4 == 0 and c 16-byte (fp32) or
- * 8-byte (bf16) aligned; bf16 output is fastest with ldc % 8 == 0, N % 8 == 0
- * and c 16-byte aligned.  Other shapes run a slower bounds-checked kernel.
+ * scale rows with ld_scales % 4 == 0, ldc % 4 == 0, c 16-byte (fp32) or
+ * 8-byte (bf16) aligned, and an operand span per 256-row tile below 4 GiB
+ * (255 * ld_codes + K/2 < 2^32 and 255 * ld_scales + K/32 < 2^32, for both
+ * operands); bf16 output is fastest with ldc % 8 == 0, N % 8 == 0 and c
+ * 16-byte aligned.  Other shapes run a slower bounds-checked kernel.
  */
 mx_status mx_gemm(const mx_qtensor *a, const mx_qtensor *b, int64_t M, int64_t N, int64_t K,
                   mx_grid grid, int32_t block, void *c, int64_t ldc, mx_out out,

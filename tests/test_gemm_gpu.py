@@ -221,3 +221,41 @@ def test_fprop_qkv_full_size_sampled():
     c_ref, g = gemm_ref(*rx, *rw, 4096, "e2m1", rows=rows, cols=cols)
     assert_gemm_close(y32[rows][:, cols].cpu().numpy(), c_ref, g, "fprop fp32")
     assert_gemm_close(y16[rows][:, cols].float().cpu().numpy(), c_ref, g, "fprop bf16", bf16=True)
+
+
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("m,n,k", [(512, 512, 1024), (300, 200, 160)])
+def test_nan_scale_blocks_give_nan_outputs(grid, m, n, k):
+    """Blocks with the E8M0 NaN scale (0xFF), as the quantizer writes them for non-finite input (all codes
+    zero): every output whose dot product meets such a block is NaN, every other output is within tolerance
+    of the oracle (whose decode maps 0xFF to NaN).  Whole-tile kernel (512^3) and bounds-checked kernel."""
+    announce("gemm NaN scales %s %dx%dx%d" % (grid, m, n, k))
+    rng = np.random.default_rng(k + m)
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    for (codes, scales), count in ((a, 5), (b, 3)):
+        lines = rng.choice(codes.shape[0], count, replace=False)
+        blocks = rng.integers(0, k // 32, count)
+        for ln, bk in zip(lines, blocks):
+            scales[ln, bk] = 0xFF
+            codes[ln, 16 * bk:16 * bk + 16] = 0
+    c = run_gemm(a, b, grid)
+    c_ref, g = gemm_ref(*a, *b, k, grid)
+    nan_ref = np.isnan(c_ref)
+    assert nan_ref.sum() >= (5 * n + 3 * m) // 2
+    assert np.array_equal(np.isnan(c), nan_ref)
+    ok = ~nan_ref
+    assert_gemm_close(c[ok][None, :], c_ref[ok][None, :], g[ok][None, :], "NaN-scale gemm %s" % grid)
+
+
+def test_whole_tile_path_more_tiles_than_workgroups_full_output():
+    """4608 x 4096 x 512: 18 x 16 = 288 output tiles on 256 persistent workgroups, so some workgroups walk a
+    second round (its DMA lookahead crosses the tile boundary); every output against the oracle."""
+    announce("gemm 288 tiles full output")
+    rng = np.random.default_rng(288)
+    m, n, k = 4608, 4096, 512
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    c = run_gemm(a, b, "e2m1")
+    c_ref, g = gemm_ref(*a, *b, k, "e2m1")
+    assert_gemm_close(c, c_ref, g, "288 tiles")

@@ -74,3 +74,24 @@ def test_uniform_words_index_layout(torch_philox):
     got = uniform_words(seed, stream, idx)
     ref = torch_philox([(seed, stream, i) for i in range(10)]).reshape(-1)
     assert np.array_equal(got.astype(np.uint64), ref)
+
+
+def test_rht_signs_from_torch_philox(torch_philox):
+    """The random-sign vector of the randomized rotation: s_j = -1 iff bit j of word 0 of the draw with
+    counter (0, 0, 2, 0) (offset 0, subsequence 2) under key had_seed; one draw serves H16 and H32."""
+    from oracle.hadamard import rht_signs, sylvester, rotate_lines
+    seeds = [0, 1, 20250, 2 ** 64 - 1, 0x123456789ABCDEF]
+    ref = torch_philox([(s, 2, 0) for s in seeds])
+    for seed, words in zip(seeds, ref):
+        w0 = int(words[0])
+        for n in (16, 32):
+            want = np.array([-1 if (w0 >> j) & 1 else 1 for j in range(n)])
+            assert np.array_equal(rht_signs(n, seed), want), (seed, n)
+    # the signs multiply the INPUTS before H: rotating the unit vector e_j gives s_j * column j of H / sqrt(n)
+    s = rht_signs(32, 20250)
+    h = sylvester(32)
+    for j in (0, 5, 31):
+        e = np.zeros((1, 32), dtype=np.uint16)
+        e[0, j] = 0x3F80                                  # bf16 1.0
+        y = rotate_lines(e, 32, s)[0].astype(np.float64)
+        assert np.array_equal(np.sign(y), s[j] * h[:, j]), j

@@ -105,7 +105,9 @@ def test_llama_k_projection_training_step(grid):
 def test_fused_projections_match_separate_linears():
     """q/k/v and gate/up as fused projections: with RTNE on every operand each part's Fprop columns and Wgrad
     rows equal the separate linears' GEMMs bit for bit (part widths are multiples of the 256-wide output tiles
-    and of the 32-value blocks, so every tile and block sees the same data in the same order)."""
+    and of the 32-value blocks, so every tile and block sees the same data in the same order).  The fused
+    Dgrad contracts over all parts' output features at once: its dX is the sum of the parts' dX, up to the
+    fp32 summation order and the bf16 roundings of the parts (checked as a norm: within 1%)."""
     from block_scaled_fp4_hadamard_amd.linear_step import LlamaBlockStep, FUSED_PROJECTIONS
     from block_scaled_fp4_hadamard_amd.synth import LLAMA_LINEARS
     announce("fused projections against separate linears")
@@ -134,3 +136,7 @@ def test_fused_projections_match_separate_linears():
             assert torch.equal(y[:, off:off + o].view(torch.int16), sep.out[p]["y"].view(torch.int16)), p
             assert torch.equal(dw[off:off + o].view(torch.int32), sep.out[p]["dw"].view(torch.int32)), p
             off += o
+        dx = fused.out[name]["dx"].float()
+        parts_dx = sum(sep.out[p]["dx"].float() for p in parts)
+        rel = float(torch.linalg.norm(dx - parts_dx) / torch.linalg.norm(dx))
+        assert rel < 1e-2 if len(parts) > 1 else rel == 0.0, (name, rel)
