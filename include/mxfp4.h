@@ -33,12 +33,13 @@
  * (emax 2 for E2M1, 0 for E1M2; amax 0 gives -127); v = |y| / 2^e goes to the
  * grid by round-to-nearest-even (ties to the even code, saturating at the top
  * level) or by stochastic rounding: with lo <= v < hi adjacent levels and
- * f = (v - lo) / (hi - lo), round up iff floor(f * 2^22) + (u >> 10) >= 2^22
- * (add-and-truncate on the top 22 bits of u), where u is word
- * (i mod 4) of Philox4x32-10(key = seed, counter = (i div 4, stream, 0)) for
- * the element at index i of the output's logical row-major order (row-wise:
- * r*cols + c, stream 0; column-wise: c*rows + r, stream 1).  A block holding a
- * non-finite value gets scale 0xFF and codes 0.
+ * f = (v - lo) / (hi - lo), round up iff floor(f * 2^16) + r >= 2^16
+ * (add-and-truncate on 16 random bits: unbiased up to 2^-16 of a step), where
+ * r is the 16-bit half (i mod 2, low half first) of word (i mod 8) / 2 of
+ * Philox4x32-10(key = seed, counter = (i div 8, stream, 0)) for the element at
+ * index i of the output's logical row-major order (row-wise: r*cols + c,
+ * stream 0; column-wise: c*rows + r, stream 1).  A block holding a non-finite
+ * value gets scale 0xFF and codes 0.
  *
  * The rotation (mx_hadamard_quantize): y = RN32(RN32(S) * RN32(1/sqrt(n)))
  * per aligned chunk of n = 16 or 32 along the quantization axis, where S is

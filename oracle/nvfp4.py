@@ -16,9 +16,10 @@ Readings (the page gives the structure, not the arithmetic):
 * s_i = the E4M3 value nearest to amax_16 / (6 * s_o) (ties to the even
   code; above 448 saturates to 448; the quotient taken exactly);
 * y = RN32(RN64(x * RN64(1 / (s_i * s_o)))), then the MX cast of y at unit
-  scale: E2M1 by RTNE or by the 22-bit stochastic rule, saturating at 6, sign
-  in bit 3, element 2j in the low nibble, Philox word of element i of the
-  output's logical row-major order (stream 0 row-wise, 1 column-wise);
+  scale: E2M1 by RTNE or by the 16-bit stochastic rule of oracle.quantize,
+  saturating at 6, sign in bit 3, element 2j in the low nibble, the 16-bit
+  Philox draw of element i of the output's logical row-major order (stream 0
+  row-wise, 1 column-wise);
 * s_i = 0 (all-zero inner block, or underflow) gives codes that keep only the
   sign; s_o = 0 (an all-zero outer block) gives s_i = 0;
 * an outer block holding Inf or NaN gets s_o = NaN, inner scales 0x7F and zero
@@ -127,15 +128,15 @@ def nvfp4_quantize_ref(x_bits, axis="row", rounding=RTNE, seed=0, lines=None):
 def _cast_unit_scale(y, rounding, seed, stream, ids, k):
     """E2M1 codes of y at scale 2^0 (RTNE or SR), packed; element indices as in oracle.quantize."""
     from .quantize import rtne_magnitude_codes, sr_magnitude_codes
-    from .philox import uniform_words
+    from .philox import uniform_halfwords
     yy = np.where(np.isfinite(y), y, 0).astype(np.float64)
     v = np.abs(yy)
     if rounding == RTNE:
         mag = rtne_magnitude_codes(v, E2M1)
     else:
         idx = ids.astype(np.uint64)[:, None] * np.uint64(k) + np.arange(k, dtype=np.uint64)[None, :]
-        u = uniform_words(seed, stream, idx).reshape(v.shape)
-        mag = sr_magnitude_codes(v, u, E2M1)
+        r = uniform_halfwords(seed, stream, idx).reshape(v.shape)
+        mag = sr_magnitude_codes(v, r, E2M1)
     codes4 = ((np.signbit(y).astype(np.uint8) << 3) | mag).astype(np.uint8)
     return (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
 

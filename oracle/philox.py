@@ -62,17 +62,21 @@ STREAM_COL_SR = 1
 STREAM_RHT_SIGNS = 2
 
 
-def uniform_words(seed, stream, index):
-    """The 32-bit uniform word of element ``index`` (int array) in ``stream``.
+def uniform_halfwords(seed, stream, index):
+    """The 16-bit uniform draw of element ``index`` (int array) in ``stream``.
 
-    Element i takes word (i mod 4) of Philox4x32-10 with key (seed lo, seed hi)
-    and counter (lo(i div 4), hi(i div 4), stream, 0).
+    One Philox4x32-10 call (key (seed lo, seed hi), counter (lo(i div 8),
+    hi(i div 8), stream, 0)) yields 128 bits, i.e. eight 16-bit draws: element i
+    takes word (i mod 8) div 2 of the call, its low half for even i and its high
+    half for odd i.
     """
     index = np.asarray(index, dtype=np.uint64)
     k0, k1 = split64(np.uint64(seed))
-    blk = index >> np.uint64(2)
+    blk = index >> np.uint64(3)
     b0, b1 = split64(blk)
     w = philox4x32_10(b0, b1, np.uint64(stream), np.uint64(0), k0, k1)
-    lane = (index & np.uint64(3)).astype(np.int64)
-    words = np.stack(w, axis=0)  # (4, ...)
-    return np.take_along_axis(words, lane[None, ...], axis=0)[0]
+    word = ((index & np.uint64(7)) >> np.uint64(1)).astype(np.int64)
+    words = np.stack(w, axis=0).astype(np.uint64)  # (4, ...)
+    picked = np.take_along_axis(words, word[None, ...], axis=0)[0]
+    shift = (index & np.uint64(1)) * np.uint64(16)
+    return ((picked >> shift) & np.uint64(0xFFFF)).astype(np.uint32)

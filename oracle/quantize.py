@@ -28,14 +28,16 @@ design notes):
 * RTNE: nearest level, a tie goes to the even code, anything above the top
   level saturates to it;
 * SR: with lo <= v < hi adjacent levels, frac = (v - lo) / (hi - lo) and
-  P = floor(frac * 2^22), the magnitude rounds up iff P + floor(u / 2^10) >= 2^22
-  for the element's 32-bit Philox word u, i.e. floor(frac + r) with r the top
-  22 bits of u read as a fraction; v at or above the top level saturates;
-* the Philox word of the element at index i of the output's logical row-major
+  P = floor(frac * 2^16), the magnitude rounds up iff P + r >= 2^16 for the
+  element's 16-bit draw r, i.e. floor(frac + r / 2^16) on a 16-bit truncated
+  frac; v at or above the top level saturates.  The probability of rounding
+  up is P / 2^16, so E[SR(v)] = v up to less than 2^-16 of a step;
+* the 16-bit draw of the element at index i of the output's logical row-major
   order (row r, column c of a row-wise output: i = r*cols + c; a column-wise
-  output is indexed in the transposed tensor: i = c*rows + r) is word i mod 4
-  of Philox4x32-10(key = seed, counter = (i div 4, stream)), stream 0 for the
-  row-wise output and 1 for the column-wise one;
+  output is indexed in the transposed tensor: i = c*rows + r) is half i mod 2
+  (low half first) of word (i mod 8) div 2 of Philox4x32-10(key = seed,
+  counter = (i div 8, stream)), stream 0 for the row-wise output and 1 for the
+  column-wise one: one call serves eight elements;
 * a tail block shorter than 32 (oracle only) takes its absmax over the values
   present; a missing high nibble is 0.
 """
@@ -46,7 +48,7 @@ import numpy as np
 from .formats import (E2M1, E1M2, EMAX, E8M0_BIAS, E8M0_NAN, SCALE_EXP_MIN, SCALE_EXP_MAX,
                       bf16_bits_to_f64, levels)
 from .hadamard import rotate_lines, rht_signs, HADAMARD_SIZES
-from .philox import uniform_words, STREAM_ROW_SR, STREAM_COL_SR
+from .philox import uniform_halfwords, STREAM_ROW_SR, STREAM_COL_SR
 
 RTNE = "rtne"
 SR = "sr"
@@ -63,15 +65,15 @@ def rtne_magnitude_codes(v, grid):
     return np.where(tie & (idx % 2 == 1), idx + 1, idx).astype(np.uint8)
 
 
-def sr_magnitude_codes(v, u, grid):
-    """Stochastic rounding of v >= 0 onto the grid, given 32-bit words u (same shape).
+def sr_magnitude_codes(v, r, grid):
+    """Stochastic rounding of v >= 0 onto the grid, given 16-bit draws r (same shape).
 
-    Round up from the largest level lo <= v iff floor(frac * 2^22) + (u >> 10)
-    >= 2^22: frac = (v - lo) / (hi - lo) truncated to 22 bits, plus a 22-bit
-    uniform fraction (the top bits of u), carried into the integer part.  The
-    probability of rounding up is floor(frac * 2^22) / 2^22, so E[SR(v)] = v up
-    to less than 2^-22 of a step ("Résumé Technique : TetraJet-v2", section 2:
-    unbiased stochastic rounding).
+    Round up from the largest level lo <= v iff floor(frac * 2^16) + r >= 2^16:
+    frac = (v - lo) / (hi - lo) truncated to 16 bits, plus a 16-bit uniform
+    fraction, carried into the integer part.  The probability of rounding up
+    is floor(frac * 2^16) / 2^16, so E[SR(v)] = v up to less than 2^-16 of a
+    step ("Résumé Technique : TetraJet-v2", section 2: unbiased stochastic
+    rounding).
 
     v - lo is exact in float64: either lo = 0, or lo >= v/2 (Sterbenz), since
     adjacent levels of both grids are at most a factor 2 apart.
@@ -82,9 +84,8 @@ def sr_magnitude_codes(v, u, grid):
     lo_c = np.minimum(lo, len(lv) - 2)
     width = lv[lo_c + 1] - lv[lo_c]
     frac = (v - lv[lo_c]) / width                   # width is a power of two: exact
-    p22 = np.floor(frac * 2.0 ** 22)                # 22-bit fixed-point probability
-    r22 = (np.asarray(u, dtype=np.uint64) >> np.uint64(10)).astype(np.float64)
-    up = p22 + r22 >= 2.0 ** 22
+    p16 = np.floor(frac * 2.0 ** 16)                # 16-bit fixed-point probability
+    up = p16 + np.asarray(r, dtype=np.float64) >= 2.0 ** 16
     code = np.where(top, len(lv) - 1, lo + up.astype(np.int64))
     return code.astype(np.uint8)
 
@@ -151,8 +152,8 @@ def quantize_values(y, grid=E2M1, rounding=RTNE, seed=0, stream=STREAM_ROW_SR, b
         ids = np.arange(lines) if line_ids is None else np.asarray(line_ids)
         idx = (ids.astype(np.uint64)[:, None] * np.uint64(length)
                + np.arange(nblk * block, dtype=np.uint64)[None, :])
-        u = uniform_words(seed, stream, idx).reshape(lines, nblk, block)
-        mag = sr_magnitude_codes(v, u, grid)
+        r = uniform_halfwords(seed, stream, idx).reshape(lines, nblk, block)
+        mag = sr_magnitude_codes(v, r, grid)
     sign = np.signbit(yb).astype(np.uint8)
     codes4 = (sign << 3) | mag
     codes4 = np.where(finite_blk[:, :, None], codes4, 0).astype(np.uint8)
@@ -195,12 +196,12 @@ def quantize_ref(x_bits, axis="row", grid=E2M1, rounding=RTNE, seed=0,
 # ---------------------------------------------------------------------------
 # Scalar, exact-arithmetic forms of the cast, for pinning the array code.
 
-def cast_scalar(v, grid, rounding, u=0):
+def cast_scalar(v, grid, rounding, r=0):
     """Magnitude code of one exact value v >= 0 (a Fraction), by exhaustive search.
 
     RTNE: the level nearest to v; on a tie the even code.  SR: round up from
-    the largest level <= v iff floor(frac * 2^22) + (u >> 10) >= 2^22.  Above
-    the top level both saturate.
+    the largest level <= v iff floor(frac * 2^16) + r >= 2^16 for the 16-bit
+    draw r.  Above the top level both saturate.
     """
     lv = [Fraction(x) for x in levels(grid)]
     v = Fraction(v)
@@ -211,5 +212,5 @@ def cast_scalar(v, grid, rounding, u=0):
         return best
     lo = max(k for k in range(len(lv)) if lv[k] <= v)
     frac = (v - lv[lo]) / (lv[lo + 1] - lv[lo])
-    p22 = (frac * 2 ** 22).numerator // (frac * 2 ** 22).denominator
-    return lo + (1 if p22 + (int(u) >> 10) >= 2 ** 22 else 0)
+    p16 = (frac * 2 ** 16).numerator // (frac * 2 ** 16).denominator
+    return lo + (1 if p16 + int(r) >= 2 ** 16 else 0)

@@ -150,27 +150,29 @@ def test_sr_array_matches_scalar(grid):
     top = 8.0 if grid == F.E2M1 else 2.0
     v = np.concatenate([rng.uniform(0, top, 4000), np.ldexp(rng.uniform(0.5, 1, 200), -rng.integers(10, 140, 200))])
     v = v.astype(np.float32).astype(np.float64)
-    u = rng.integers(0, 2 ** 32, v.size, dtype=np.uint64)
-    got = sr_magnitude_codes(v, u, grid)
-    want = np.array([cast_scalar(Fraction(float(x)), grid, SR, int(w)) for x, w in zip(v, u)])
+    r = rng.integers(0, 2 ** 16, v.size, dtype=np.uint64)
+    got = sr_magnitude_codes(v, r, grid)
+    want = np.array([cast_scalar(Fraction(float(x)), grid, SR, int(w)) for x, w in zip(v, r)])
     assert np.array_equal(got, want)
 
 
 def test_sr_threshold_is_floor_of_fixed_point_probability():
-    # frac = 1/3 cannot be held in 22 bits: P22 = floor(2^22 / 3) = 1398101, and v rounds up iff the top 22
-    # bits of u reach 2^22 - P22 = 2796203
-    v = np.array([0.5 + 0.5 / 3])      # float64 rounding of 2/3 keeps P22's floor value
-    assert int(np.floor((v[0] - 0.5) / 0.5 * 2 ** 22)) == 1398101
-    edge = 2796203 << 10
-    assert sr_magnitude_codes(v, np.array([edge]), F.E2M1)[0] == 2
-    assert sr_magnitude_codes(v, np.array([edge + 1023]), F.E2M1)[0] == 2
-    assert sr_magnitude_codes(v, np.array([edge - 1]), F.E2M1)[0] == 1
+    # frac = 1/3 cannot be held in 16 bits: P16 = floor(2^16 / 3) = 21845, and v rounds up iff the 16-bit
+    # draw reaches 2^16 - P16 = 43691
+    v = np.array([0.5 + 0.5 / 3])      # float64 rounding of 2/3 keeps P16's floor value
+    assert int(np.floor((v[0] - 0.5) / 0.5 * 2 ** 16)) == 21845
+    assert sr_magnitude_codes(v, np.array([43691]), F.E2M1)[0] == 2
+    assert sr_magnitude_codes(v, np.array([65535]), F.E2M1)[0] == 2
+    assert sr_magnitude_codes(v, np.array([43690]), F.E2M1)[0] == 1
     assert sr_magnitude_codes(v, np.array([0]), F.E2M1)[0] == 1
-    assert sr_magnitude_codes(np.array([1.0]), np.array([0xFFFFFFFF]), F.E2M1)[0] == 2   # on a level: unchanged
-    # the probability is the 22-bit truncated fraction: exactly P22 of the 2^22 values of u >> 10 round up
-    r = np.arange(0, 2 ** 22, 97, dtype=np.uint64) << np.uint64(10)
+    assert sr_magnitude_codes(np.array([1.0]), np.array([65535]), F.E2M1)[0] == 2   # on a level: unchanged
+    # the probability is the 16-bit truncated fraction: exactly P16 of the 2^16 draws round up, so the
+    # bias is 1/3 - 21845 / 2^16 = 1 / (3 * 2^16), below 2^-16 of the step
+    r = np.arange(0, 2 ** 16, dtype=np.uint64)
     ups = sr_magnitude_codes(np.full(r.shape, v[0]), r, F.E2M1) == 2
-    assert ups.sum() == np.count_nonzero((r >> np.uint64(10)) >= 2796203)
+    assert ups.sum() == 21845
+    bias = Fraction(1, 3) - Fraction(int(ups.sum()), 2 ** 16)
+    assert 0 < bias < Fraction(1, 2 ** 16)
 
 
 # ---- exact fp32 rounding of wide sums ------------------------------------------

@@ -14,7 +14,7 @@ import tempfile
 import numpy as np
 import pytest
 
-from oracle.philox import philox4x32_10, split64, uniform_words
+from oracle.philox import philox4x32_10, split64, uniform_halfwords
 
 KAT_SRC = r"""
 #include <ATen/core/PhiloxRNGEngine.h>
@@ -67,13 +67,20 @@ def test_philox_matches_torch_header(torch_philox):
         assert np.array_equal(got, want), (seed, sub, off)
 
 
-def test_uniform_words_index_layout(torch_philox):
-    # element i uses word i%4 of the call with offset i//4 in its stream
+def test_uniform_halfwords_index_layout(torch_philox):
+    # element i takes the (i % 2) half (low first) of word (i % 8) // 2 of the call with offset i // 8
     seed, stream = 0xDEADBEEF12345, 1
-    idx = np.arange(40, dtype=np.uint64)
-    got = uniform_words(seed, stream, idx)
-    ref = torch_philox([(seed, stream, i) for i in range(10)]).reshape(-1)
-    assert np.array_equal(got.astype(np.uint64), ref)
+    idx = np.arange(80, dtype=np.uint64)
+    got = uniform_halfwords(seed, stream, idx).astype(np.uint64)
+    words = torch_philox([(seed, stream, i) for i in range(10)]).reshape(-1)      # 4 words per call
+    want = np.array([(int(words[4 * (i // 8) + (i % 8) // 2]) >> (16 * (i % 2))) & 0xFFFF for i in range(80)])
+    assert np.array_equal(got, want.astype(np.uint64))
+    # indices far from zero use both counter words
+    big = np.array([2 ** 35 + 13, 2 ** 40 + 6], dtype=np.uint64)
+    got = uniform_halfwords(seed, 0, big)
+    for i, g in zip(big, got):
+        w = torch_philox([(seed, 0, int(i) // 8)])[0]
+        assert g == (int(w[(int(i) % 8) // 2]) >> (16 * (int(i) % 2))) & 0xFFFF
 
 
 def test_rht_signs_from_torch_philox(torch_philox):
