@@ -17,9 +17,12 @@ synthetic tensors of the real shapes, resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
-with each family's achieved HBM GB/s or MFMA TFLOP/s; `mxnorm` times the fused
-MXNorm + row-wise cast launch apart from the step, `nvfp4` the double-block quantizer; `roofline` is the dominant
-kernel's; `cpu_baseline` is the CPU oracle on a bounded sample.
+with each family's achieved HBM GB/s or MFMA TFLOP/s; `step_e1m2` is the same
+step on the uniform grid; `workloads` times the quantizer-only workload (cold
+and hot, RTNE and SR), the fused-QKV Fprop GEMM and the MLP Dgrad and Wgrad
+GEMMs on their own; `mxnorm` times the fused MXNorm + row-wise cast launch,
+`nvfp4` the double-block quantizer; `roofline` is the dominant kernel's;
+`cpu_baseline` is the CPU oracle on bounded samples.
 """
 import argparse
 import json
@@ -81,17 +84,39 @@ def load_traffic(family):
         return None
 
 
-def cpu_baseline(tokens=4096):
-    """The oracle on one q-projection linear (4096x4096) with `tokens` tokens: the same
-    quantization recipe and the three GEMMs, timed on this host's cores."""
-    import numpy as np
-    from oracle.recipe import linear_layer_operands, gemm_of
-    from block_scaled_fp4_hadamard_amd import synth
+def host_cpu():
+    """The host's CPU model, its logical CPU count, and how many of them this process may run on."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_baseline(tokens=4096):
+    """The oracle, as it stands, timed on this host on bounded samples of the benchmarked work.
+
+    value: one q-projection linear (4096x4096) with `tokens` tokens through the block's recipe (quantize X, W
+    and dY along both axes with RHT H32, SR on dY, then the three float64 GEMMs), as GEMM TFLOP/s, with the
+    BLAS threads the host gives.  quantizer_1t: the quantizer-only workload's first 1024 rows (H32, both axes)
+    on one thread, RTNE and SR, as algorithmic GB/s.  gemm_1t / gemm_all: the float64 GEMM oracle (C and the
+    tolerance scale G) on a 1024x1024x4096 sample, on one thread and on all threads."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle.recipe import linear_layer_operands, gemm_of
+    from oracle.quantize import quantize_ref
+    from oracle.gemm import gemm_ref
+    from block_scaled_fp4_hadamard_amd import synth
+    cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     rng = np.random.default_rng(1)
     x = synth.activation(tokens, synth.D_MODEL, rng)
     w = synth.weight(synth.D_MODEL, synth.D_MODEL, rng)
@@ -102,9 +127,30 @@ def cpu_baseline(tokens=4096):
         gemm_of(ops, which)
     dt = time.time() - t0
     flops = 3 * 2 * tokens * synth.D_MODEL * synth.D_MODEL
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": "q projection 4096x4096 with %d tokens: quantize X, W, dY on both axes (RHT H32, SR on dY) "
-                      "+ Fprop/Dgrad/Wgrad fp64 GEMMs; %.1f s" % (tokens, dt)}
+    res = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": "q projection 4096x4096 with %d tokens: quantize X, W, dY on both axes (RHT H32, SR on dY) "
+                     "+ Fprop/Dgrad/Wgrad fp64 GEMMs; %.1f s on %d BLAS threads" % (tokens, dt, cores)}
+    res.update(host_cpu())
+    xq = synth.quant_x()[:1024]
+    qbytes = xq.size * 2 + 2 * (xq.size // 2 + xq.size // 32)
+    with threadpool_limits(limits=1):
+        q1 = {}
+        for rounding, seed in (("rtne", 0), ("sr", 1)):
+            t0 = time.time()
+            quantize_ref(xq, "both", rounding=rounding, seed=seed, had_n=32)
+            q1[rounding] = round(qbytes / (time.time() - t0) / 1e9, 5)
+        res["quantizer_1t"] = {"GB/s": q1, "sample": "1024x4096 of the quantizer-only X, H32, both axes",
+                               "threads": 1}
+    a = ops["x"]["row"][0][:1024], ops["x"]["row"][1][:1024]
+    b = ops["w"]["row"][0][:1024], ops["w"]["row"][1][:1024]
+    gflop = 2 * 1024 * 1024 * 4096
+    for key, lim in (("gemm_1t", 1), ("gemm_all", None)):
+        with threadpool_limits(limits=lim):
+            t0 = time.time()
+            gemm_ref(*a, *b, 4096, "e2m1")
+            res[key] = {"TFLOP/s": round(gflop / (time.time() - t0) / 1e12, 6),
+                        "threads": 1 if lim == 1 else int(cores), "sample": "1024x1024x4096 fp64 C and G"}
+    return res
 
 
 def measure_mxnorm(tensors, dev, reps=30):
@@ -176,6 +222,127 @@ def measure_block16(tensors, dev, reps=30):
     return res
 
 
+def time_step(step, steps, stream):
+    """Time `steps` whole steps with one event before each launch: (ms per step, per-family sums)."""
+    import numpy as np
+    import torch
+    nl = len(step.launches)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for i, L in enumerate(step.launches):
+            evs[s][i].record(stream)
+            L.fn()
+        evs[s][nl].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = float(np.mean([evs[s][0].elapsed_time(evs[s][nl]) for s in range(steps)]))
+    fam = {}
+    for i, L in enumerate(step.launches):
+        d = [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]
+        f = fam.setdefault(L.label, {"launches": 0, "ms": 0.0, "bytes": 0, "flops": 0})
+        f["launches"] += 1
+        f["ms"] += float(np.mean(d))
+        f["bytes"] += L.bytes
+        f["flops"] += L.flops
+    return ms_per_step, fam
+
+
+def family_table(fam):
+    kernels = {}
+    for label, f in fam.items():
+        k = {"launches_per_step": f["launches"], "ms_per_step": round(f["ms"], 4),
+             "us_per_launch": round(f["ms"] / f["launches"] * 1e3, 2)}
+        if f["flops"]:
+            k["TFLOP/s"] = round(f["flops"] / (f["ms"] * 1e-3) / 1e12, 1)
+            k["frac_mfma"] = round(k["TFLOP/s"] / FP4_PEAK_TFLOPS, 4)
+        else:
+            k["GB/s"] = round(f["bytes"] / (f["ms"] * 1e-3) / 1e9, 1)
+            k["frac_hbm"] = round(k["GB/s"] / HBM_PEAK_GBS, 4)
+        kernels[label] = k
+    return kernels
+
+
+def time_us(fn, reps, stream):
+    """Mean microseconds per call of fn(i), i = 0 .. reps-1, from events on the launch stream."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def gemm_entry(us, m, n, k, what):
+    tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+    return {"workload": what, "M": m, "N": n, "K": k, "us": round(us, 2), "TFLOP/s": round(tf, 1),
+            "frac_mfma": round(tf / FP4_PEAK_TFLOPS, 4)}
+
+
+def measure_configs(dev, stream):
+    """The quantizer and GEMM workloads at Llama-3.1-8B shapes, each timed on its own.
+
+    quantizer: an 8192x4096 activation (0.1% of the channels x50), deterministic H32, both axes from one
+    launch, RTNE and Philox SR (seed 1).  Cold: five copies of the tensor (335 MB, more than the 256 MB
+    last-level cache) and five output sets in rotation; hot: one.  fprop_qkv: Y = X W^T, 8192x6144x4096, H16
+    on K, RTNE, bf16 out.  mlp_dgrad: dY (Laplace, spikes) times W_down as printed, 8192x4096x14336, RTNE,
+    bf16 out.  mlp_wgrad: dY^T X, 14336x14336x8192, both operands column-wise with SR, fp32 out.
+    """
+    import numpy as np
+    import torch
+    from block_scaled_fp4_hadamard_amd import api, synth
+
+    def gpu(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+    out = {}
+    x = gpu(synth.quant_x())
+    rows, cols = x.shape
+    nbytes = rows * cols * 2 + 2 * (rows * cols // 2 + rows * cols // 32)
+    xs = [x] + [x.clone() for _ in range(4)]
+    q = {}
+    for rounding, seed in (("rtne", 0), ("sr", 1)):
+        sets = [(api.empty_qtensor(rows, cols, dev), api.empty_qtensor(cols, rows, dev)) for _ in xs]
+
+        def run(i, rounding=rounding, seed=seed, sets=sets, n=len(xs)):
+            api.quantize(xs[i % n], axis="both", rounding=rounding, seed=seed, had_n=32, had_kind="det",
+                         row_out=sets[i % n][0], col_out=sets[i % n][1])
+        run(0)
+        cold = time_us(run, 50, stream)
+        hot = time_us(lambda i: run(0), 50, stream)
+        gbs = nbytes / (cold * 1e-6) / 1e9
+        q[rounding] = {"us_cold": round(cold, 2), "us_hot": round(hot, 2), "GB/s": round(gbs, 1),
+                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    out["quantizer"] = dict(workload="X 8192x4096 bf16, H32 deterministic, E2M1, row- and column-wise outputs "
+                                     "from one launch", bytes_per_call=nbytes, **q)
+    del xs, sets
+
+    d = synth.fprop_qkv()
+    qx = api.quantize(gpu(d["x"]), axis="row", had_n=16)["row"]
+    qw = api.quantize(gpu(d["w"]), axis="row", had_n=16)["row"]
+    y = torch.empty((8192, 6144), dtype=torch.bfloat16, device=dev)
+    api.gemm(qx, qw, out=y)
+    us = time_us(lambda i: api.gemm(qx, qw, out=y), 20, stream)
+    out["fprop_qkv"] = gemm_entry(us, 8192, 6144, 4096, "Y = X W^T, H16 on K, RTNE, bf16 out")
+    del d, qx, qw, y
+
+    d = synth.mlp()
+    qd = api.quantize(gpu(d["dy"]), axis="col", rounding="sr", seed=4000)
+    qdr = api.quantize(gpu(d["dy"]), axis="row")["row"]
+    qw = api.quantize(gpu(d["w"]), axis="row")["row"]
+    qx = api.quantize(gpu(d["x"]), axis="col", rounding="sr", seed=4002)["col"]
+    dx = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
+    api.gemm(qdr, qw, out=dx)
+    us = time_us(lambda i: api.gemm(qdr, qw, out=dx), 20, stream)
+    out["mlp_dgrad"] = gemm_entry(us, 8192, 4096, 14336, "dX = dY W_down (shapes as printed), RTNE, bf16 out")
+    dw = torch.empty((14336, 14336), dtype=torch.float32, device=dev)
+    api.gemm(qd["col"], qx, out=dw)
+    us = time_us(lambda i: api.gemm(qd["col"], qx, out=dw), 10, stream)
+    out["mlp_wgrad"] = gemm_entry(us, 14336, 14336, 8192, "dW = dY^T X, column-wise SR operands, fp32 out")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -208,40 +375,11 @@ def main():
 
     # timed region: K whole steps, one event before each launch and one at the end
     stream = torch.cuda.current_stream(dev)
-    nl = len(step.launches)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     wall0 = time.time()
-    for s in range(args.steps):
-        for i, L in enumerate(step.launches):
-            evs[s][i].record(stream)
-            L.fn()
-        evs[s][nl].record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, fam = time_step(step, args.steps, stream)
     wall = time.time() - wall0
-    step_ms = [evs[s][0].elapsed_time(evs[s][nl]) for s in range(args.steps)]
-    ms_per_step = float(np.mean(step_ms))
     log("timed %d steps: %.3f ms/step (wall %.3f ms/step)" % (args.steps, ms_per_step, wall / args.steps * 1e3))
-
-    fam = {}
-    for i, L in enumerate(step.launches):
-        d = [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]
-        f = fam.setdefault(L.label, {"launches": 0, "ms": 0.0, "bytes": 0, "flops": 0})
-        f["launches"] += 1
-        f["ms"] += float(np.mean(d))
-        f["bytes"] += L.bytes
-        f["flops"] += L.flops
-    kernels = {}
-    for label, f in fam.items():
-        k = {"launches_per_step": f["launches"], "ms_per_step": round(f["ms"], 4),
-             "us_per_launch": round(f["ms"] / f["launches"] * 1e3, 2)}
-        if f["flops"]:
-            k["TFLOP/s"] = round(f["flops"] / (f["ms"] * 1e-3) / 1e12, 1)
-            k["frac_mfma"] = round(k["TFLOP/s"] / FP4_PEAK_TFLOPS, 4)
-        else:
-            k["GB/s"] = round(f["bytes"] / (f["ms"] * 1e-3) / 1e9, 1)
-            k["frac_hbm"] = round(k["GB/s"] / HBM_PEAK_GBS, 4)
-        kernels[label] = k
+    kernels = family_table(fam)
     dom = max(fam, key=lambda lb: fam[lb]["ms"])
     f = fam[dom]
     avg_s = f["ms"] / f["launches"] * 1e-3
@@ -256,6 +394,18 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom}
     mxnorm = measure_mxnorm(tensors, dev)
     block16 = measure_block16(tensors, dev)
+    # the same step on the other grid (the uniform E1M2 grid's GEMMs run on the FP6 matrix path)
+    other = "e1m2" if args.grid == "e2m1" else "e2m1"
+    step2 = LlamaBlockStep(tensors, Recipe(grid=other, fuse=not args.unfused))
+    step2.run()
+    ms2, fam2 = time_step(step2, max(3, args.steps // 2), stream)
+    other_step = {"grid": other, "ms_per_step": round(ms2, 4),
+                  "value": round(step2.flops / (ms2 * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                  "kernels": family_table(fam2)}
+    del step2
+    log("%s step: %.3f ms" % (other, ms2))
+    configs = measure_configs(dev, stream)
+    log("workloads timed")
     qms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("quant"))
     gms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("gemm"))
     quant_gbs = step.quant_bytes / (qms * 1e-3) / 1e9
@@ -288,6 +438,8 @@ def main():
         "gemm": {"TFLOP/s": round(gemm_tf, 1), "frac_mfma": round(gemm_tf / FP4_PEAK_TFLOPS, 4),
                  "ms_per_step": round(gms, 4)},
         "kernels": kernels,
+        "step_" + other: other_step,
+        "workloads": configs,
         "mxnorm": mxnorm,
         "nvfp4": block16,
         "roofline": roof,

@@ -20,7 +20,10 @@ __device__ __forceinline__ uint32_t e8m0_scale_bits(uint32_t byte) {
 // 4-bit code of one value y of a block with scale byte `byte` (finite y):
 // sign bit 3, magnitude code = |y| / 2^(byte-127) on the grid, rounded by
 // RTNE, or (SR) up from the level below iff floor(frac * 2^22) + (u >> 10)
-// >= 2^22 for the element's random word u; saturating at the top level.
+// >= 2^22; saturating at the top level.  The element's 16-bit draw r comes in
+// the top half of u (u = r << 16), which makes the rule floor(frac * 2^16) + r
+// >= 2^16 exactly: floor(frac 2^22) + 2^6 r >= 2^22 <=> floor(frac 2^16) + r
+// >= 2^16, r being an integer.
 template <int GRID, int ROUND>
 __device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u) {
   typedef float v2f __attribute__((ext_vector_type(2)));
@@ -29,7 +32,7 @@ __device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, yy, 0.0f, sc, 0) & 0xFu;
   } else if constexpr (GRID == MX_GRID_E2M1) {
     // gfx950's stochastic fp4 conversion applies exactly this rule (the
-    // element's own word; the pair's second value is a placeholder, and the
+    // element's own draw; the pair's second value is a placeholder, and the
     // other result bytes are not kept)
     return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (v2f){yy, 0.0f}, u, sc, 0) & 0xFu;
   } else {
@@ -55,9 +58,6 @@ __device__ __forceinline__ uint32_t scale_byte(uint32_t expf) {
   return expf > kEmax ? expf - kEmax : 0u;
 }
 
-// Cast one 32-element block y[] of finite values into 4 code dwords; returns
-// the scale byte.  For SR, y[i] draws Philox word i % 4 of counter block
-// ctr + i / 4 (stream `stream`, key k0:k1).
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies on a 128-bit counter, Weyl-bumped 64-bit key.  The key
@@ -92,15 +92,16 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
   return U4{c0, c1, c2, c3};
 }
 
-// Philox4x32-10 of the four counters (ctr + q, stream, 0), q = 0..3 (ctr is
+// Philox4x32-10 of the NC counters (ctr + q, stream, 0), q = 0..NC-1 (ctr is
 // the 64-bit block index in the first two counter words), run in lockstep:
-// the four dependency chains of multiplies interleave instead of waiting on
-// one another.
-__device__ __forceinline__ void philox4x32_10_x4(uint64_t ctr, uint32_t stream, uint32_t k0, uint32_t k1,
-                                                 U4 (&out)[4]) {
-  uint32_t c0[4], c1[4], c2[4], c3[4];
+// the dependency chains of multiplies interleave instead of waiting on one
+// another.
+template <int NC>
+__device__ __forceinline__ void philox4x32_10_xn(uint64_t ctr, uint32_t stream, uint32_t k0, uint32_t k1,
+                                                 U4 (&out)[NC]) {
+  uint32_t c0[NC], c1[NC], c2[NC], c3[NC];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NC; ++q) {
     const uint64_t b = ctr + (uint64_t)q;
     c0[q] = (uint32_t)b;
     c1[q] = (uint32_t)(b >> 32);
@@ -110,7 +111,7 @@ __device__ __forceinline__ void philox4x32_10_x4(uint64_t ctr, uint32_t stream, 
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NC; ++q) {
       const uint64_t p0 = (uint64_t)c0[q] * kPhiloxM0;
       const uint64_t p1 = (uint64_t)c2[q] * kPhiloxM1;
       const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1[q], k0);
@@ -124,7 +125,36 @@ __device__ __forceinline__ void philox4x32_10_x4(uint64_t ctr, uint32_t stream, 
     k1 += kPhiloxW1;
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) out[q] = U4{c0[q], c1[q], c2[q], c3[q]};
+  for (int q = 0; q < NC; ++q) out[q] = U4{c0[q], c1[q], c2[q], c3[q]};
+}
+
+// The stochastic-rounding operands of 8 * NC consecutive elements (element
+// index 8 ctr8 + e, e = 0 .. 8 NC - 1): element e takes the 16-bit half e % 2
+// (low half first) of word (e % 8) / 2 of the call with counter ctr8 + e / 8,
+// placed in the top half of its operand (cast_one takes u = r << 16).
+template <int NC>
+__device__ __forceinline__ void sr_draws(uint64_t ctr8, uint32_t stream, uint32_t k0, uint32_t k1,
+                                         uint32_t (&u)[8 * NC]) {
+  U4 r[NC];
+  philox4x32_10_xn<NC>(ctr8, stream, k0, k1, r);
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[8 * q + 2 * j] = w[j] << 16;
+      u[8 * q + 2 * j + 1] = w[j] & 0xFFFF0000u;
+    }
+  }
+}
+
+// The operand of one element at index i (see sr_draws).
+__device__ __forceinline__ uint32_t sr_draw_one(uint64_t i, uint32_t stream, uint32_t k0, uint32_t k1) {
+  const uint64_t g = i >> 3;
+  const U4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), stream, 0u, k0, k1);
+  const uint32_t j = ((uint32_t)i & 7u) >> 1;
+  const uint32_t w = (j & 2u) ? ((j & 1u) ? r.w : r.z) : ((j & 1u) ? r.y : r.x);
+  return (i & 1u) ? (w & 0xFFFF0000u) : (w << 16);
 }
 
 // ---------------------------------------------------------------------------

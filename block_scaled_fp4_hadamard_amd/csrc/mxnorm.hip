@@ -149,17 +149,7 @@ __device__ __forceinline__ uint32_t cast8(const uint4& v, uint32_t xmax, float r
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], sc, 3);
   } else {
     uint32_t u[8] = {};
-    if constexpr (ROUND == MX_ROUND_SR) {
-      const uint64_t i0 = (uint64_t)elem >> 2;                // element index / 4 (elem % 8 == 0)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const U4 q = philox4x32_10((uint32_t)(i0 + h), (uint32_t)((i0 + h) >> 32), 0u, 0u, k0, k1);
-        u[4 * h] = q.x;
-        u[4 * h + 1] = q.y;
-        u[4 * h + 2] = q.z;
-        u[4 * h + 3] = q.w;
-      }
-    }
+    if constexpr (ROUND == MX_ROUND_SR) sr_draws<1>((uint64_t)elem >> 3, 0u, k0, k1, u);   // elem % 8 == 0
 #pragma unroll
     for (int i = 0; i < 8; ++i) r |= cast_one<GRID, ROUND>(y[i], byte, u[i]) << (4 * i);
   }

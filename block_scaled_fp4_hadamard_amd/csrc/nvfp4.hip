@@ -98,22 +98,13 @@ __device__ __forceinline__ int64_t tile_div(int64_t a, int64_t b) {
 // One inner block of 16 values.  get(k) gives value k as float bits (the
 // bf16 pattern in the high half); amax16 / amax128 are the |x| maxima of the
 // inner and outer block as bf16 magnitude patterns (>= 0x7F80: Inf/NaN
-// present).  ctr: Philox counter of value 0 (its element index / 4).
+// present).  ctr8: Philox counter of value 0 (its element index / 8).
 // Returns the 8 code bytes; sets the scale byte and (double block) s_o.
 template <int MODE, int GRID, int ROUND, class Get>
-__device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax128, uint64_t ctr, uint32_t stream,
+__device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax128, uint64_t ctr8, uint32_t stream,
                                          uint32_t k0, uint32_t k1, uint32_t& scale, float& so_out) {
   uint32_t u[16] = {};
-  if constexpr (ROUND == MX_ROUND_SR) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const U4 r = philox4x32_10((uint32_t)(ctr + h), (uint32_t)((ctr + h) >> 32), stream, 0u, k0, k1);
-      u[4 * h] = r.x;
-      u[4 * h + 1] = r.y;
-      u[4 * h + 2] = r.z;
-      u[4 * h + 3] = r.w;
-    }
-  }
+  if constexpr (ROUND == MX_ROUND_SR) sr_draws<2>(ctr8, stream, k0, k1, u);
   uint32_t w[2] = {0u, 0u};
   bool zero_codes;
   if constexpr (MODE == 0) {
@@ -191,8 +182,8 @@ __device__ __forceinline__ void block16_row(const Block16Params& p, int64_t tile
   auto get = [&](int k) { return (k & 1) ? (v[k >> 1] & 0xFFFF0000u) : (v[k >> 1] << 16); };
   uint32_t scale;
   float so = 0.0f;
-  const uint64_t ctr = ((uint64_t)row * (uint64_t)p.cols + (uint64_t)pos0) >> 2;
-  const uint2 c = quant16<MODE, GRID, ROUND>(get, amax16, amax128, ctr, 0u, (uint32_t)p.seed,
+  const uint64_t ctr8 = ((uint64_t)row * (uint64_t)p.cols + (uint64_t)pos0) >> 3;
+  const uint2 c = quant16<MODE, GRID, ROUND>(get, amax16, amax128, ctr8, 0u, (uint32_t)p.seed,
                                             (uint32_t)(p.seed >> 32), scale, so);
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   __builtin_nontemporal_store(u32x2{c.x, c.y}, (u32x2*)(p.codes + row * p.ld_codes + pos0 / 2));
@@ -241,8 +232,8 @@ __device__ __forceinline__ void block16_col(const Block16Params& p, int64_t tile
     uint32_t scale;
     float so = 0.0f;
     const int64_t line = col + j;
-    const uint64_t ctr = ((uint64_t)line * (uint64_t)p.rows + (uint64_t)row) >> 2;
-    const uint2 c = quant16<MODE, GRID, ROUND>(get, amax16, amax128, ctr, 1u, k0, k1, scale, so);
+    const uint64_t ctr8 = ((uint64_t)line * (uint64_t)p.rows + (uint64_t)row) >> 3;
+    const uint2 c = quant16<MODE, GRID, ROUND>(get, amax16, amax128, ctr8, 1u, k0, k1, scale, so);
     *(uint2*)(cbase + j * p.ld_codes) = c;
     sbase[j * p.ld_scales] = (uint8_t)scale;
     if (MODE == 1 && (lane & 7) == 0) obase[j * p.ld_outer] = so;

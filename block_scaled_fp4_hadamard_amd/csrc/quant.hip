@@ -37,9 +37,9 @@
 //
 // The E2M1 casts use gfx950's scaled fp4 conversions, which divide by the
 // power-of-two scale given as a float and saturate: ties to even for RTNE,
-// and for stochastic rounding the add-and-truncate rule above with the top
-// 22 bits of each element's own Philox word.  The uniform grid runs in plain
-// VALU code.
+// and for stochastic rounding the add-and-truncate rule on each element's own
+// 16-bit Philox draw (eight draws per Philox call).  The uniform grid runs in
+// plain VALU code.
 //
 // Tile order is XCD-aware: workgroup w runs on XCD w % 8, and the 8 row tiles
 // of a 256x256 region are all taken by workgroups of one XCD at about the
@@ -95,8 +95,10 @@ __device__ __forceinline__ uint32_t lds_col(int c, int rbits) {
 }
 __device__ __forceinline__ uint32_t lds_off(int r, int c) { return (uint32_t)(r * kRowBytes) + lds_col(c, r & 9); }
 
+// Cast one 32-element block y[] of finite values into 4 code dwords; returns
+// the scale byte.  For SR, ctr8 is the block's first element index / 8.
 template <int GRID, int ROUND>
-__device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ctr, uint32_t stream, uint32_t k0,
+__device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ctr8, uint32_t stream, uint32_t k0,
                                                uint32_t k1, uint32_t (&w)[4]) {
   float m = 0.0f;
 #pragma unroll
@@ -116,16 +118,9 @@ __device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ct
     }
   } else {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {                 // 16 outputs (four Philox blocks) at a time
+    for (int hh = 0; hh < 2; ++hh) {                 // 16 outputs (two Philox calls) at a time
       uint32_t u[16] = {};
-      if constexpr (ROUND == MX_ROUND_SR) {
-        U4 r[4];
-        philox4x32_10_x4(ctr + 4 * hh, stream, k0, k1, r);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u[4 * q + 0] = r[q].x; u[4 * q + 1] = r[q].y; u[4 * q + 2] = r[q].z; u[4 * q + 3] = r[q].w;
-        }
-      }
+      if constexpr (ROUND == MX_ROUND_SR) sr_draws<2>(ctr8 + 2 * hh, stream, k0, k1, u);
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         uint32_t r = 0;
@@ -253,9 +248,9 @@ __device__ __forceinline__ uint32_t split_low(uint32_t w, uint32_t t2) {
 
 // Cast one lane's half of a block: y[0..16) are outputs 16(l / 32) .. +15,
 // the other half is in lane l ^ 32.  Writes 2 code dwords; returns the scale
-// byte.  For SR, y[i] draws Philox word i % 4 of counter block ctr + i / 4.
+// byte.  For SR, ctr8 is the element index of y[0] / 8.
 template <int GRID, int ROUND>
-__device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int lane, uint64_t ctr, uint32_t stream,
+__device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int lane, uint64_t ctr8, uint32_t stream,
                                                     uint32_t k0, uint32_t k1, uint32_t (&w)[2]) {
   float m = 0.0f;
 #pragma unroll
@@ -277,14 +272,7 @@ __device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int la
     }
   } else {
     uint32_t u[16] = {};
-    if constexpr (ROUND == MX_ROUND_SR) {
-      U4 r[4];
-      philox4x32_10_x4(ctr, stream, k0, k1, r);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u[4 * q + 0] = r[q].x; u[4 * q + 1] = r[q].y; u[4 * q + 2] = r[q].z; u[4 * q + 3] = r[q].w;
-      }
-    }
+    if constexpr (ROUND == MX_ROUND_SR) sr_draws<2>(ctr8, stream, k0, k1, u);
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       uint32_t r = 0;
@@ -407,13 +395,13 @@ __device__ __forceinline__ void exact_fixup(const QuantParams& p, const uint8_t*
     const bool col_axis = (ent >> 15) != 0u;
     const int owner = (int)(ent & 0x7FFFu);
     float y;
-    uint64_t ctr;
+    uint64_t first;                                  // element index of the block's output 0
     uint8_t* codes;
     uint8_t* scale;
     if (col_axis) {
       y = special_value<HAD>([&](int j) { return (uint32_t)*(const uint16_t*)(buf + lds_off(j, owner)); }, i, mask);
       const int64_t col = col0 + owner;
-      ctr = ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2;
+      first = (uint64_t)col * (uint64_t)p.rows + (uint64_t)row0;
       codes = p.col_codes + col * p.ld_col_codes + row0 / 2;
       scale = p.col_scales + col * p.ld_col_scales + row0 / 32;
     } else {
@@ -421,7 +409,7 @@ __device__ __forceinline__ void exact_fixup(const QuantParams& p, const uint8_t*
       y = special_value<HAD>([&](int j) { return (uint32_t)*(const uint16_t*)(buf + lds_off(r, 32 * k + j)); }, i,
                              mask);
       const int64_t row = row0 + r, c0 = col0 + 32 * k;
-      ctr = ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2;
+      first = (uint64_t)row * (uint64_t)p.cols + (uint64_t)c0;
       codes = p.row_codes + row * p.ld_row_codes + c0 / 2;
       scale = p.row_scales + row * p.ld_row_scales + c0 / 32;
     }
@@ -431,11 +419,7 @@ __device__ __forceinline__ void exact_fixup(const QuantParams& p, const uint8_t*
     const bool nonfinite = mb >= 0x7F800000u;
     const uint32_t byte = nonfinite ? 0xFFu : scale_byte<GRID>(mb >> 23);
     uint32_t u = 0;
-    if constexpr (ROUND == MX_ROUND_SR) {
-      const uint64_t g = ctr + (uint64_t)(i >> 2);     // element i draws word i % 4 of block ctr + i / 4
-      const U4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), col_axis ? 1u : 0u, 0u, k0, k1);
-      u = (i & 2) ? ((i & 1) ? r.w : r.z) : ((i & 1) ? r.y : r.x);
-    }
+    if constexpr (ROUND == MX_ROUND_SR) u = sr_draw_one(first + (uint64_t)i, col_axis ? 1u : 0u, k0, k1);
     uint32_t word = nonfinite ? 0u : cast_one<GRID, ROUND>(y, byte, u) << (4 * (i & 7));
     word |= (uint32_t)__shfl_xor((int)word, 1);
     word |= (uint32_t)__shfl_xor((int)word, 2);
@@ -598,7 +582,7 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
           mask, y);
       uint32_t w[4];
       const uint32_t byte =
-          cast_block<GRID, ROUND>(y, ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 2, 0u, k0, k1, w);
+          cast_block<GRID, ROUND>(y, ((uint64_t)row * (uint64_t)p.cols + (uint64_t)c0) >> 3, 0u, k0, k1, w);
       const bool valid = row < p.rows && c0 < p.cols;
       if (valid) *(uint4*)(p.row_codes + row * p.ld_row_codes + c0 / 2) = uint4{w[0], w[1], w[2], w[3]};
       store_row_scales(p.row_scales + row * p.ld_row_scales + col0 / 32, k, byte, wide_scales && full_width, valid);
@@ -619,7 +603,7 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
           mask, y);
       uint32_t w[4];
       const uint32_t byte =
-          cast_block<GRID, ROUND>(y, ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 2, 1u, k0, k1, w);
+          cast_block<GRID, ROUND>(y, ((uint64_t)col * (uint64_t)p.rows + (uint64_t)row0) >> 3, 1u, k0, k1, w);
       if (col < p.cols) {
         *(uint4*)(p.col_codes + col * p.ld_col_codes + row0 / 2) = uint4{w[0], w[1], w[2], w[3]};
         p.col_scales[col * p.ld_col_scales + row0 / 32] = (uint8_t)byte;
@@ -671,7 +655,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const int64_t rl = row0 + 8 * wave + (n >> 3);
     uint8_t* const cbase = p.row_codes + rl * p.ld_row_codes + col0 / 2 + 16 * (n & 7) + 8 * hl;
     uint8_t* const sbase = p.row_scales + rl * p.ld_row_scales + col0 / 32;
-    const uint64_t ctr0 = (((uint64_t)rl * (uint64_t)p.cols + (uint64_t)(col0 + 32 * (n & 7))) >> 2) + 4 * hl;
+    const uint64_t ctr0 = (((uint64_t)rl * (uint64_t)p.cols + (uint64_t)(col0 + 32 * (n & 7))) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       __builtin_amdgcn_sched_barrier(0);
@@ -691,8 +675,10 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       const int64_t row = row0 + r, c0 = col0 + 32 * k;
       const bool valid = interior || (row < p.rows && c0 < p.cols);
       uint32_t w[2];
-      // counter of the lane's first output: (row * cols + c0) / 4 + 4 hl, and cols % 8 == 0
-      const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)p.cols, 0u, k0, k1, w);
+      // counter of the lane's first output: (row * cols + c0) / 8 + 2 hl; group g is 4 rows further, and
+      // cols % 8 == 0
+      const uint32_t byte =
+          cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)(p.cols >> 1), 0u, k0, k1, w);
       typedef unsigned int u2v __attribute__((ext_vector_type(2)));
       if (valid) *(u2v*)(cbase + 4 * g * p.ld_row_codes) = u2v{w[0], w[1]};
       store_row_scales(sbase + 4 * g * p.ld_row_scales, k, byte, wide_scales && full_width, valid && hl == 0);
@@ -704,7 +690,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const int64_t cl = col0 + 64 * wave + n;
     uint8_t* const ccbase = p.col_codes + cl * p.ld_col_codes + row0 / 2 + 8 * hl;
     uint8_t* const csbase = p.col_scales + cl * p.ld_col_scales + row0 / 32;
-    const uint64_t cctr0 = (((uint64_t)cl * (uint64_t)p.rows + (uint64_t)row0) >> 2) + 4 * hl;
+    const uint64_t cctr0 = (((uint64_t)cl * (uint64_t)p.rows + (uint64_t)row0) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       __builtin_amdgcn_sched_barrier(0);
@@ -732,8 +718,8 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       mfma_block_sums<PARTS>(ha, part, c, y);
       const int64_t cc = cl + 32 * g;
       uint32_t w[2];
-      // counter: (cc * rows + row0) / 4 + 4 hl, and rows % 32 == 0 here
-      const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, cctr0 + (uint64_t)(8 * g) * (uint64_t)p.rows, 1u, k0,
+      // counter: (cc * rows + row0) / 8 + 2 hl with cc 32 g columns further, and rows % 32 == 0 here
+      const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, cctr0 + (uint64_t)(4 * g) * (uint64_t)p.rows, 1u, k0,
                                                          k1, w);
       if (cc < p.cols) {
         *(uint2*)(ccbase + 32 * g * p.ld_col_codes) = uint2{w[0], w[1]};
