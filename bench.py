@@ -14,6 +14,7 @@ synthetic tensors of the real shapes, resident in HBM before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--unfused]
     python bench.py --calibrate-copy BYTES     (device copies of BYTES, for traffic-counter scaling)
+    python bench.py --workloads-only           (only the per-workload timings, for profiler runs)
 
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
@@ -50,6 +51,10 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     ap.add_argument("--unfused", action="store_true", help="one GEMM per linear instead of fused qkv and gate_up")
+    ap.add_argument("--workloads-only", action="store_true",
+                    help="time only the quantizer-only, fused-QKV and MLP workloads (for profiler runs)")
+    ap.add_argument("--workload", action="append", choices=list(WORKLOADS),
+                    help="with --workloads-only: just these workloads (repeatable)")
     return ap.parse_args()
 
 
@@ -281,7 +286,10 @@ def gemm_entry(us, m, n, k, what):
             "frac_mfma": round(tf / FP4_PEAK_TFLOPS, 4)}
 
 
-def measure_configs(dev, stream):
+WORKLOADS = ("quantizer", "fprop_qkv", "mlp_dgrad", "mlp_wgrad")
+
+
+def measure_configs(dev, stream, only=None):
     """The quantizer and GEMM workloads at Llama-3.1-8B shapes, each timed on its own.
 
     quantizer: an 8192x4096 activation (0.1% of the channels x50), deterministic H32, both axes from one
@@ -297,7 +305,41 @@ def measure_configs(dev, stream):
     def gpu(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
     out = {}
-    x = gpu(synth.quant_x())
+    want = set(only or WORKLOADS)
+    if "quantizer" in want:
+        out["quantizer"] = measure_quantizer(gpu(synth.quant_x()), dev, stream)
+    if "fprop_qkv" in want:
+        d = synth.fprop_qkv()
+        qx = api.quantize(gpu(d["x"]), axis="row", had_n=16)["row"]
+        qw = api.quantize(gpu(d["w"]), axis="row", had_n=16)["row"]
+        y = torch.empty((8192, 6144), dtype=torch.bfloat16, device=dev)
+        api.gemm(qx, qw, out=y)
+        us = time_us(lambda i: api.gemm(qx, qw, out=y), 20, stream)
+        out["fprop_qkv"] = gemm_entry(us, 8192, 6144, 4096, "Y = X W^T, H16 on K, RTNE, bf16 out")
+        del d, qx, qw, y
+    if "mlp_dgrad" in want or "mlp_wgrad" in want:
+        d = synth.mlp()
+    if "mlp_dgrad" in want:
+        qdr = api.quantize(gpu(d["dy"]), axis="row")["row"]
+        qw = api.quantize(gpu(d["w"]), axis="row")["row"]
+        dx = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
+        api.gemm(qdr, qw, out=dx)
+        us = time_us(lambda i: api.gemm(qdr, qw, out=dx), 20, stream)
+        out["mlp_dgrad"] = gemm_entry(us, 8192, 4096, 14336, "dX = dY W_down (shapes as printed), RTNE, bf16 out")
+        del qdr, qw, dx
+    if "mlp_wgrad" in want:
+        qd = api.quantize(gpu(d["dy"]), axis="col", rounding="sr", seed=4000)["col"]
+        qx = api.quantize(gpu(d["x"]), axis="col", rounding="sr", seed=4002)["col"]
+        dw = torch.empty((14336, 14336), dtype=torch.float32, device=dev)
+        api.gemm(qd, qx, out=dw)
+        us = time_us(lambda i: api.gemm(qd, qx, out=dw), 10, stream)
+        out["mlp_wgrad"] = gemm_entry(us, 14336, 14336, 8192, "dW = dY^T X, column-wise SR operands, fp32 out")
+    return out
+
+
+def measure_quantizer(x, dev, stream):
+    """The quantizer-only workload (see measure_configs)."""
+    from block_scaled_fp4_hadamard_amd import api
     rows, cols = x.shape
     nbytes = rows * cols * 2 + 2 * (rows * cols // 2 + rows * cols // 32)
     xs = [x] + [x.clone() for _ in range(4)]
@@ -314,33 +356,8 @@ def measure_configs(dev, stream):
         gbs = nbytes / (cold * 1e-6) / 1e9
         q[rounding] = {"us_cold": round(cold, 2), "us_hot": round(hot, 2), "GB/s": round(gbs, 1),
                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    out["quantizer"] = dict(workload="X 8192x4096 bf16, H32 deterministic, E2M1, row- and column-wise outputs "
-                                     "from one launch", bytes_per_call=nbytes, **q)
-    del xs, sets
-
-    d = synth.fprop_qkv()
-    qx = api.quantize(gpu(d["x"]), axis="row", had_n=16)["row"]
-    qw = api.quantize(gpu(d["w"]), axis="row", had_n=16)["row"]
-    y = torch.empty((8192, 6144), dtype=torch.bfloat16, device=dev)
-    api.gemm(qx, qw, out=y)
-    us = time_us(lambda i: api.gemm(qx, qw, out=y), 20, stream)
-    out["fprop_qkv"] = gemm_entry(us, 8192, 6144, 4096, "Y = X W^T, H16 on K, RTNE, bf16 out")
-    del d, qx, qw, y
-
-    d = synth.mlp()
-    qd = api.quantize(gpu(d["dy"]), axis="col", rounding="sr", seed=4000)
-    qdr = api.quantize(gpu(d["dy"]), axis="row")["row"]
-    qw = api.quantize(gpu(d["w"]), axis="row")["row"]
-    qx = api.quantize(gpu(d["x"]), axis="col", rounding="sr", seed=4002)["col"]
-    dx = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
-    api.gemm(qdr, qw, out=dx)
-    us = time_us(lambda i: api.gemm(qdr, qw, out=dx), 20, stream)
-    out["mlp_dgrad"] = gemm_entry(us, 8192, 4096, 14336, "dX = dY W_down (shapes as printed), RTNE, bf16 out")
-    dw = torch.empty((14336, 14336), dtype=torch.float32, device=dev)
-    api.gemm(qd["col"], qx, out=dw)
-    us = time_us(lambda i: api.gemm(qd["col"], qx, out=dw), 10, stream)
-    out["mlp_wgrad"] = gemm_entry(us, 14336, 14336, 8192, "dW = dY^T X, column-wise SR operands, fp32 out")
-    return out
+    return dict(workload="X 8192x4096 bf16, H32 deterministic, E2M1, row- and column-wise outputs from one launch",
+                bytes_per_call=nbytes, **q)
 
 
 def main():
@@ -360,6 +377,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.workloads_only:
+        print(json.dumps({"workloads": measure_configs(dev, torch.cuda.current_stream(dev), args.workload)}),
+              flush=True)
+        return 0
     t0 = time.time()
     host = synth.llama_block(args.tokens)
     tensors = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in host.items()}

@@ -36,25 +36,27 @@ __device__ __forceinline__ int swz(int row, int piece) {  // 16-byte piece posit
   return (piece ^ ((row >> 1) & 3)) * 16;
 }
 
-// E1M2 code nibbles (8 per dword) -> 6-bit E2M3 codes packed LSB first.
+// E1M2 code nibbles (8 per dword) -> 6-bit E2M3 codes packed LSB first:
+// nibble (s, k) becomes (s << 5) | (k << 1).  The 8 nibbles of a dword are
+// spread from a 4-bit to a 6-bit pitch in three steps (halves 8 bits apart,
+// then quarters 4 bits, then odd nibbles 2 bits), each a shift and two masks
+// on a 64-bit value, and the fields are then formed in place.  The 48-bit
+// chunks of the four dwords concatenate into the six output dwords.
+__device__ __forceinline__ uint64_t e1m2_chunk(uint32_t d) {
+  uint64_t x = d;
+  x = (x & 0x000000000000FFFFull) | ((x << 8) & 0x000000FFFF000000ull);
+  x = (x & 0x00000000FF0000FFull) | ((x << 4) & 0x00000FF0000FF000ull);
+  x = (x & 0x000000F00F00F00Full) | ((x << 2) & 0x00003C03C03C03C0ull);
+  return ((x & 0x0000208208208208ull) << 2) | ((x & 0x00001C71C71C71C7ull) << 1);
+}
 __device__ __forceinline__ void e1m2_to_e2m3(const uint32_t (&in)[4], uint32_t (&out)[6]) {
-  uint64_t acc = 0;
-  int nbits = 0, o = 0;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t n = (in[d] >> (4 * q)) & 0xFu;
-      const uint64_t f6 = ((n & 8u) << 2) | ((n & 7u) << 1);
-      acc |= f6 << nbits;
-      nbits += 6;
-      if (nbits >= 32) {
-        out[o++] = (uint32_t)acc;
-        acc >>= 32;
-        nbits -= 32;
-      }
-    }
-  }
+  const uint64_t c0 = e1m2_chunk(in[0]), c1 = e1m2_chunk(in[1]), c2 = e1m2_chunk(in[2]), c3 = e1m2_chunk(in[3]);
+  out[0] = (uint32_t)c0;
+  out[1] = (uint32_t)(c0 >> 32) | ((uint32_t)c1 << 16);
+  out[2] = (uint32_t)(c1 >> 16);
+  out[3] = (uint32_t)c2;
+  out[4] = (uint32_t)(c2 >> 32) | ((uint32_t)c3 << 16);
+  out[5] = (uint32_t)(c3 >> 16);
 }
 
 // Two floats to packed bf16 (a in the low half) by gfx950's packed conversion:
@@ -219,18 +221,29 @@ __device__ __forceinline__ uint32_t dpp_xor2_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
 }
 
-template <int OUT, int MT, int NT>
+// An accumulator element read out of its AGPR where it is used (the 4 x 4
+// accumulators stay in AGPRs; letting the compiler copy them all into VGPRs
+// ahead of the stores spills).
+__device__ __forceinline__ float agpr_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+template <int OUT, int MT, int NT, bool W16>
 __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row0, int64_t col0, int lane,
-                                                const v16f (&acc)[MT][NT], bool wide16) {
+                                                const v16f (&acc)[MT][NT]) {
   const int half = lane >> 5, quad = (lane & 31) >> 2, k = lane & 3;
-  if (OUT == MX_OUT_F32 || !wide16) {
+  if constexpr (OUT == MX_OUT_F32 || !W16) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = NT > 2 ? agpr_read(acc[i][j][4 * g + e]) : acc[i][j][4 * g + e];
           transpose4(v, lane);
           const int64_t row = row0 + i * 32 + 8 * g + 4 * half + k;
           const int64_t col = col0 + j * 32 + 4 * quad;
@@ -243,6 +256,9 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
             __builtin_nontemporal_store(u2v{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])},
                                         (u2v*)((uint16_t*)p.c + row * p.ldc + col));
           }
+          // with the accumulators in AGPRs, keep each group's reads next to its store instead of letting all
+          // of them be hoisted into VGPRs at once
+          if constexpr (NT > 2) __builtin_amdgcn_sched_barrier(0);
         }
   } else {
     // bf16, 16 bytes per lane.  Each 4x4 block is rounded first (P0 = rows 0-1, P1 = rows 2-3 of the
@@ -268,17 +284,19 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
       q0 = __builtin_amdgcn_perm(r, a, sel_q0);
       q1 = __builtin_amdgcn_perm(r, b, sel_q1);
     };
-    static_assert(NT == 2, "a row of the wave's tile is two 32-column halves");
+    static_assert(NT % 2 == 0, "the wave's tile rows pair 32-column halves");
+#pragma unroll
+    for (int jp = 0; jp < NT; jp += 2)
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int g = 0; g < 4; g += 2) {
-        // rows R = 8g + 4h + k and R + 8, each in the left (j = 0) and right (j = 1) half
+        // rows R = 8g + 4h + k and R + 8, each in the left (j = jp) and right (j = jp + 1) half
         uint32_t a0[2], a1[2], b0[2], b1[2];
-        rows4(acc[i][0], g, a0[0], a0[1]);
-        rows4(acc[i][1], g, a1[0], a1[1]);
-        rows4(acc[i][0], g + 1, b0[0], b0[1]);
-        rows4(acc[i][1], g + 1, b1[0], b1[1]);
+        rows4(acc[i][jp], g, a0[0], a0[1]);
+        rows4(acc[i][jp + 1], g, a1[0], a1[1]);
+        rows4(acc[i][jp], g + 1, b0[0], b0[1]);
+        rows4(acc[i][jp + 1], g + 1, b1[0], b1[1]);
         // an even quad keeps the left half and gets its partner's left columns; an odd quad keeps the
         // right half (lanes l ^ 4; bit mode: and 0x1F, xor 4)
         uint32_t ra[2], rb[2];
@@ -290,9 +308,10 @@ __device__ __forceinline__ void store_tile_wide(const GemmParams& p, int64_t row
         typedef unsigned int u4v __attribute__((ext_vector_type(4)));
         const u4v da = qodd ? u4v{ra[0], ra[1], a1[0], a1[1]} : u4v{a0[0], a0[1], ra[0], ra[1]};
         const u4v db = qodd ? u4v{rb[0], rb[1], b1[0], b1[1]} : u4v{b0[0], b0[1], rb[0], rb[1]};
-        const uint8_t* base = wave_uniform((const uint8_t*)p.c + ((row0 + i * 32 + 8 * g) * p.ldc + col0) * 2);
+        const uint8_t* base = wave_uniform((const uint8_t*)p.c + ((row0 + i * 32 + 8 * g) * p.ldc + col0 + 32 * jp) * 2);
         __builtin_nontemporal_store(da, (__attribute__((address_space(1))) u4v*)(base + loff));
         __builtin_nontemporal_store(db, (__attribute__((address_space(1))) u4v*)(base + loff + 16 * p.ldc));
+        if constexpr (NT > 2) __builtin_amdgcn_sched_barrier(0);
       }
   }
 }
@@ -325,15 +344,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Whole-tile path.  A 512-lane workgroup (8 waves: 2 along M x 4 along N, each
-// 128 x 64 = 4 x 2 MFMA tiles, two waves per SIMD) owns a 256 x 256 block of C.
+// Whole-tile path.  A workgroup owns a 256 x 256 block of C, as 8 waves (2
+// along M x 4 along N, each 128 x 64 = 4 x 2 MFMA tiles, two waves per SIMD;
+// NT = 2) or as 4 waves (2 x 2, each 128 x 128 = 4 x 4 MFMA tiles with the
+// accumulators in AGPRs, one wave per SIMD; NT = 4), which reads a third
+// fewer fragment bytes from LDS per MFMA.
 // K advances 256 per step: every row contributes one whole 128-byte line per
 // step, moved global -> LDS by DMA (global_load_lds_dwordx4) into one of two
 // 68 KB stages while the MFMAs consume the other.  Within a step the four
 // 64-deep K quarters are software pipelined: the fragments of quarter q+1 are
 // read from LDS while the MFMAs of quarter q run (two fragment register sets),
 // and the barrier of the next step sits behind the last quarter's MFMAs.
-constexpr int kFullThreads = 512;
+template <int NT>
+constexpr int full_threads() { return NT == 2 ? 512 : 256; }
 constexpr int kRowBytes = 128;            // 256 fp4 elements per row per K step
 constexpr int kFullStageBytes = kBM * kRowBytes;
 
@@ -341,9 +364,10 @@ __device__ __forceinline__ int swz8(int row, int piece) {  // 16-byte slot withi
   return (piece ^ ((row >> 1) & 7)) * 16;
 }
 
+template <int NT>
 struct Frags {
-  uint4 a[4], b[2];    // raw 16-byte code pieces (32 elements each)
-  uint32_t sa[4], sb[2];   // raw scale dwords (4 blocks); the lane's byte is picked at the MFMA
+  uint4 a[4], b[NT];         // raw 16-byte code pieces (32 elements each)
+  uint32_t sa[4], sb[NT];    // raw scale dwords (4 blocks); the lane's byte is picked at the MFMA
 };
 
 // fragments of K quarter q (64 deep) for the wave's 4 x 2 tiles.  Tile rows
@@ -353,9 +377,10 @@ struct Frags {
 // step).  A lane's block in quarter q is 2q + half; past the edge its codes
 // are zeros in LDS and its scale dwords may be stale or never copied, so it
 // takes a stand-in scale (all bytes 127): the products stay exact zeros.
-__device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const uint8_t* b, const uint32_t* sa,
+template <int NT>
+__device__ __forceinline__ void load_quarter(Frags<NT>& f, const uint8_t* a, const uint8_t* b, const uint32_t* sa,
                                              const uint32_t* sb, int q, int r0, int c0, int lane, int vb,
-                                             const Frags& prev) {
+                                             const Frags<NT>& prev) {
   const int half = lane >> 5, lrow = lane & 31;
   const int off = lrow * kRowBytes + swz8(lrow, 2 * q + half);
   // quarters 1 and 3 use the same scale dword as 0 and 2: taken from the previous quarter's fragments
@@ -365,7 +390,7 @@ __device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const u
     f.sa[i] = (q & 1) ? prev.sa[i] : sa[(q >> 1) * kBM + r0 + 32 * i + lrow];
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NT; ++j) {
     f.b[j] = *(const uint4*)(b + (c0 + 32 * j) * kRowBytes + off);
     f.sb[j] = (q & 1) ? prev.sb[j] : sb[(q >> 1) * kBN + c0 + 32 * j + lrow];
   }
@@ -374,7 +399,7 @@ __device__ __forceinline__ void load_quarter(Frags& f, const uint8_t* a, const u
 #pragma unroll
       for (int i = 0; i < 4; ++i) f.sa[i] = 0x7F7F7F7Fu;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f.sb[j] = 0x7F7F7F7Fu;
+      for (int j = 0; j < NT; ++j) f.sb[j] = 0x7F7F7F7Fu;
     }
   }
 }
@@ -393,22 +418,35 @@ __device__ __forceinline__ v8i operand(const uint4& x) {
 // the 8 MFMAs of one quarter; OPSEL picks the scale byte pair (quarters 0,2 -> 0; 1,3 -> 2)
 // Lanes 32-63 hold the odd 32-block of each 64-deep quarter: their scale is
 // one byte above the even block's, so their dwords are shifted by 8.
-template <int GRID, int OPSEL>
-__device__ __forceinline__ void mfma_quarter(const Frags& f, v16f (&acc)[4][2], int shift) {
+template <int GRID, int OPSEL, int NT>
+__device__ __forceinline__ void mfma_quarter(const Frags<NT>& f, v16f (&acc)[4][NT], int shift) {
   constexpr int kFmt = GRID == MX_GRID_E2M1 ? 4 : 2;   // 4: fp4 E2M1, 2: fp6 E2M3
-  const v8i b0 = operand<GRID>(f.b[0]), b1 = operand<GRID>(f.b[1]);
-  const int sb0 = (int)(f.sb[0] >> shift), sb1 = (int)(f.sb[1] >> shift);
+  v8i bj[NT];
+  int sbj[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    bj[j] = operand<GRID>(f.b[j]);
+    sbj[j] = (int)(f.sb[j] >> shift);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const v8i ai = operand<GRID>(f.a[i]);
     const int sai = (int)(f.sa[i] >> shift);
-    acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, b0, acc[i][0], kFmt, kFmt, OPSEL, sai, OPSEL, sb0);
-    acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, b1, acc[i][1], kFmt, kFmt, OPSEL, sai, OPSEL, sb1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, bj[j], acc[i][j], kFmt, kFmt, OPSEL, sai, OPSEL,
+                                                                  sbj[j]);
   }
   // the MFMAs are side-effect free; an empty volatile asm on their results keeps
   // them at this point of the pipeline instead of being sunk past later phases
+  // (the 4 x 4 accumulators live in AGPRs)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]));
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if constexpr (NT == 2) asm volatile("" : "+v"(acc[i][j]));
+      else asm volatile("" : "+a"(acc[i][j]));
+    }
 }
 
 // First row (or column) of tile t of a dimension of size n >= 256: the last
@@ -446,9 +484,9 @@ __device__ __forceinline__ int next_round(const TileMap& tm, const Walk& w, int 
 
 // RK: K is not a multiple of 256 (a ragged last step); a separate instance, so
 // that the whole-step kernel carries none of its register cost
-template <int GRID, int OUT, bool RK>
-__global__ void __launch_bounds__(kFullThreads, 1)
-gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) {
+template <int GRID, int OUT, bool RK, int NT, bool W16>
+__global__ void __launch_bounds__(full_threads<NT>(), 1)
+gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kFullStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kFullStageBytes];
   __shared__ __attribute__((aligned(1024))) uint32_t sSA[2][2 * kBM];    // [dword d][row]: blocks 4d..4d+3
@@ -464,7 +502,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) 
 
   const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int r0 = wm * 128, c0 = wn * 64;
+  const int r0 = wm * 128, c0 = wn * 32 * NT;
   const int nk = (int)((p.K + 255) / 256);
   const int vb_last = RK ? (int)((p.K % 256) / 32) : 8;   // blocks in the last step
   auto blocks_in = [&](int kt) { return RK && kt == nk - 1 ? vb_last : 8; };
@@ -500,7 +538,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) 
 
   // DMA of K step kt of tile (tbm, tbn) into stage st, by the waves of parity kt % 2
   auto issue = [&](int tbm, int tbn, int kt, int st) {
-    if ((wave >> 2) != (kt & 1)) return;
+    if (NT == 2 && (wave >> 2) != (kt & 1)) return;
     const int64_t m0 = tile_origin(tbm, kBM, p.M), n0 = tile_origin(tbn, kBN, p.N);
     const uint8_t* abase = wave_uniform(p.a_codes + m0 * p.lda_codes);
     const uint8_t* bbase = wave_uniform(p.b_codes + n0 * p.ldb_codes);
@@ -513,8 +551,12 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) 
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          dma16_off(abase, offa(4 * h + c) + kb, lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
-          dma16_off(bbase, offb(4 * h + c) + kb, lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+          // the copy's row base and K offset go into the wave-uniform base; the lane keeps only la / lb
+          const int e = 4 * h + c;
+          dma16_off(abase + copy_rows(e) * p.lda_codes + kb, la[e & 1],
+                    lA + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
+          dma16_off(bbase + copy_rows(e) * p.ldb_codes + kb, lb[e & 1],
+                    lB + st * kFullStageBytes + (128 * h + 8 * c) * kRowBytes);
         }
       dma4_off(sabase, osa + 8 * kt, lSA + st * (2 * kBM * 4));
       dma4_off(sabase, osa + 8 * kt + 4, lSA + st * (2 * kBM * 4) + kBM * 4);
@@ -548,18 +590,18 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) 
     }
   };
 
-  v16f acc[4][2];
+  v16f acc[4][NT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   // the tile after the current one, and the DMA cursor two K steps ahead
   int nbm = 0, nbn = 0;
   int rn = next_round(tm, w, r + 1, nbm, nbn);
-  Frags f0, f1;
+  Frags<NT> f0, f1;
   const int shift = 8 * (lane >> 5);
   issue(bm, bn, 0, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -579,15 +621,15 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) 
       const int vb = blocks_in(kt);
       load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_quarter<GRID, 0>(f0, acc, shift);
+      mfma_quarter<GRID, 0, NT>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
       load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane, vb, f1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_quarter<GRID, 2>(f1, acc, shift);
+      mfma_quarter<GRID, 2, NT>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
       load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_quarter<GRID, 0>(f0, acc, shift);
+      mfma_quarter<GRID, 0, NT>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
       const bool more = kt + 1 < nk || rn < w.rounds;
       if (more) {
@@ -602,15 +644,15 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds, bool wide16) 
         load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0), f1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      mfma_quarter<GRID, 2>(f1, acc, shift);
+      mfma_quarter<GRID, 2, NT>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile_wide<OUT, 4, 2>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc, wide16);
+    store_tile_wide<OUT, 4, NT, W16>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc);
     if (rn >= w.rounds) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
     r = rn;
@@ -680,16 +722,29 @@ gemm_general_kernel(const GemmParams p, const TileMap tm) {
   store_tile<OUT, true, 4, 4>(p, m0 + wm * 128, n0 + wn * 128, lane, acc);
 }
 
+// MFMA tiles per wave along N on the whole-tile path: 4 (four waves of 128 x 128) or 2 (eight of 128 x 64)
+constexpr int kWaveTileN = 2;
+
 template <int GRID, int OUT>
 static void launch_kind(const GemmParams& p, const TileMap& tm, bool full, dim3 g, hipStream_t s) {
   if (full) {
     // one workgroup per CU: 8 XCDs x 32 members; round r deals group r*8+xcd
     const int rounds = (tm.groups + kXcds - 1) / kXcds;
-    const dim3 g(kXcds * kGroupM * kGroupN), b(kFullThreads);
+    constexpr int NT = kWaveTileN;
+    const dim3 g(kXcds * kGroupM * kGroupN), b(full_threads<NT>());
     // bf16 rows written 16 bytes per lane need 16-byte aligned rows and tile origins
     const bool wide16 = p.ldc % 8 == 0 && p.N % 8 == 0 && (uintptr_t)p.c % 16 == 0;
-    if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false>), g, b, 0, s, p, tm, rounds, wide16);
-    else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true>), g, b, 0, s, p, tm, rounds, wide16);
+    // (fp32 rows are always written 16 bytes per lane: one instance)
+    if constexpr (OUT == MX_OUT_F32) {
+      if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, true>), g, b, 0, s, p, tm, rounds);
+      else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, true>), g, b, 0, s, p, tm, rounds);
+    } else if (wide16) {
+      if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, true>), g, b, 0, s, p, tm, rounds);
+      else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, true>), g, b, 0, s, p, tm, rounds);
+    } else {
+      if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, false>), g, b, 0, s, p, tm, rounds);
+      else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, false>), g, b, 0, s, p, tm, rounds);
+    }
   } else {
     hipLaunchKernelGGL((gemm_general_kernel<GRID, OUT>), g, dim3(kGemmThreads), 0, s, p, tm);
   }

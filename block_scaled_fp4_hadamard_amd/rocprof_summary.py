@@ -2,6 +2,9 @@
 
     python -m block_scaled_fp4_hadamard_amd.rocprof_summary stats DIR --command CMD --out FILE.md
         per-kernel dispatch count, average and total duration from a --kernel-trace run
+    python -m block_scaled_fp4_hadamard_amd.rocprof_summary counters DIR [DIR ...] --command CMDS --out FILE.md
+            [--per FAMILY=UNITS:NAME]
+        per-kernel means of every counter of --pmc runs, optionally per work unit (element, flop)
     python -m block_scaled_fp4_hadamard_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR \\
             COPY_WRITE_DIR --copy-bytes N --command CMD --out FILE.json
         HBM bytes per dispatch and kernel family from two --pmc runs (FETCH_SIZE, then WRITE_SIZE), each
@@ -112,6 +115,48 @@ def family_means(d, counter):
     return {f: (n, s / n) for f, (n, s) in fam.items()}
 
 
+def counter_table(dirs):
+    """{kernel name: {counter: (dispatches, mean per dispatch)}} over every counter in the runs' CSVs."""
+    acc = {}
+    for d in dirs:
+        per = {}
+        for f in _csvs(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                key = (int(r.get("Dispatch_Id") or 0), r["Kernel_Name"], r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name, counter), v in per.items():
+            a = acc.setdefault(name, {}).setdefault(counter, [0, 0.0])
+            a[0] += 1
+            a[1] += v
+    return {k: {c: (n, s / n) for c, (n, s) in cs.items()} for k, cs in acc.items()}
+
+
+def counters_markdown(dirs, command, title, per=None):
+    """Per-kernel means of every collected counter; with per = {family: (units per dispatch, unit name)}
+    also each counter per unit (SQ_INSTS_* per unit as lane-operations: wave instructions x 64)."""
+    tab = counter_table(dirs)
+    lines = ["# " + title, "", "Commands (repository root, one MI355X; one rocprofv3 --pmc pass each):", ""]
+    lines += ["    " + c for c in command.split(" ;; ")]
+    lines += ["", "Kernel sources hash: `%s`" % sources_hash(), ""]
+    for name in sorted(tab, key=lambda k: kernel_family(k) or "~"):
+        fam = kernel_family(name)
+        if fam is None or fam == "copy":
+            continue
+        lines += ["## `%s` (%s)" % (name[:120], fam), "", "| counter | dispatches | mean per dispatch | per unit |",
+                  "|---|---|---|---|"]
+        units = (per or {}).get(fam)
+        for c, (n, m) in sorted(tab[name].items()):
+            pu = ""
+            if units:
+                v = m * 64 if c.startswith("SQ_INSTS_") and "MOPS" not in c else m
+                if c in ("FETCH_SIZE", "WRITE_SIZE"):
+                    v = m * 1024
+                pu = "%.4g per %s" % (v / units[0], units[1])
+            lines.append("| %s | %d | %.6g | %s |" % (c, n, m, pu))
+        lines.append("")
+    return "\n".join(lines) + "\n"
+
+
 def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, command):
     cf = family_means(copy_fetch_dir, "FETCH_SIZE").get("copy")
     cw = family_means(copy_write_dir, "WRITE_SIZE").get("copy")
@@ -150,7 +195,24 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--command", required=True, help="the profiler commands, separated by ' ;; '")
+    c.add_argument("--title", default="Kernel counters")
+    c.add_argument("--per", action="append", default=[], metavar="FAMILY=UNITS:NAME",
+                   help="also report counters per unit for a kernel family (e.g. quant.rtne=33554432:element)")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        per = {}
+        for item in a.per:
+            fam, rest = item.split("=", 1)
+            units, name = rest.split(":", 1)
+            per[fam] = (float(units), name)
+        text = counters_markdown(a.dirs, a.command, a.title, per)
+        open(a.out, "w").write(text)
+        print(text)
+        return 0
     if a.cmd == "stats":
         text = stats_markdown(a.dir, a.command, a.title)
         open(a.out, "w").write(text)
