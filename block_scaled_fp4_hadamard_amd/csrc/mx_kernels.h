@@ -20,6 +20,7 @@ struct QuantParams {
   uint64_t seed;
   uint32_t sign_mask;   // bit j set: input j of every Hadamard chunk is negated
   int32_t n_row_tiles, n_col_tiles, n_row_groups;   // filled by launch_quant
+  bool fast_ok;         // output pitches allow 32-bit offsets within a tile (filled by launch_quant)
 };
 
 hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int round, bool do_row, bool do_col,

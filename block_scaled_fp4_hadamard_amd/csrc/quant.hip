@@ -467,6 +467,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// an output pointer that is the same in every lane, moved to SGPRs
+__device__ __forceinline__ uint8_t* uniform_ptr(uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
 // a pointer that is the same in every lane, moved to SGPRs
 __device__ __forceinline__ const uint16_t* wave_uniform(const uint16_t* p) {
   const uint64_t v = (uint64_t)p;
@@ -544,9 +551,9 @@ __device__ __forceinline__ void store_row_scales(uint8_t* dst, int k, uint32_t b
   if (!active) return;
   if (wide) {
     typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-    if (k == 0) *(u2v*)dst = u2v{v, hi};
+    if (k == 0) *(__attribute__((address_space(1))) u2v*)dst = u2v{v, hi};
   } else {
-    dst[k] = (uint8_t)byte;
+    ((__attribute__((address_space(1))) uint8_t*)dst)[k] = (uint8_t)byte;
   }
 }
 
@@ -641,7 +648,11 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
 //   operand (8 consecutive rows of its column) comes from two transposed LDS
 //   reads: in each 16-lane group, lane s reads 4 consecutive columns of row
 //   s / 4, and lane j receives column j of the 4 rows (ds_read_b64_tr_b16).
-template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL, int PARTS>
+// FAST: a tile wholly inside the tensor, 8-byte aligned row-scale rows, and
+// output pitches small enough for 32-bit offsets from the tile's first line
+// (QuantParams::fast_ok).  Its stores then take a wave-uniform tile base plus a
+// per-lane 32-bit offset and need no bounds tests.
+template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL, int PARTS, bool FAST>
 __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t* buf, int t, int64_t row0, int64_t col0,
                                             const uint4* htab, uint32_t t2, uint32_t t3, bool wide_scales) {
   const int lane = t & 63, wave = t >> 6, hl = lane >> 5, n = lane & 31;
@@ -655,6 +666,11 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const int64_t rl = row0 + 8 * wave + (n >> 3);
     uint8_t* const cbase = p.row_codes + rl * p.ld_row_codes + col0 / 2 + 16 * (n & 7) + 8 * hl;
     uint8_t* const sbase = p.row_scales + rl * p.ld_row_scales + col0 / 32;
+    // FAST: the same addresses as a uniform tile base and a 32-bit lane offset
+    uint8_t* const cbase_u = uniform_ptr(p.row_codes + row0 * p.ld_row_codes + col0 / 2);
+    uint8_t* const sbase_u = uniform_ptr(p.row_scales + row0 * p.ld_row_scales + col0 / 32);
+    const uint32_t coff = (uint32_t)(8 * wave + (n >> 3)) * (uint32_t)p.ld_row_codes + 16 * (n & 7) + 8 * hl;
+    const uint32_t soff = (uint32_t)(8 * wave + (n >> 3)) * (uint32_t)p.ld_row_scales;
     const uint64_t ctr0 = (((uint64_t)rl * (uint64_t)p.cols + (uint64_t)(col0 + 32 * (n & 7))) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -672,16 +688,23 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       }
       float y[16];
       mfma_block_sums<PARTS>(ha, part, c, y);
-      const int64_t row = row0 + r, c0 = col0 + 32 * k;
-      const bool valid = interior || (row < p.rows && c0 < p.cols);
       uint32_t w[2];
       // counter of the lane's first output: (row * cols + c0) / 8 + 2 hl; group g is 4 rows further, and
       // cols % 8 == 0
       const uint32_t byte =
           cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)(p.cols >> 1), 0u, k0, k1, w);
       typedef unsigned int u2v __attribute__((ext_vector_type(2)));
-      if (valid) *(u2v*)(cbase + 4 * g * p.ld_row_codes) = u2v{w[0], w[1]};
-      store_row_scales(sbase + 4 * g * p.ld_row_scales, k, byte, wide_scales && full_width, valid && hl == 0);
+      if constexpr (FAST) {
+        *(__attribute__((address_space(1))) u2v*)(cbase_u + (uint64_t)(coff + (uint32_t)(4 * g) * (uint32_t)p.ld_row_codes)) =
+            u2v{w[0], w[1]};
+        store_row_scales(sbase_u + (uint64_t)(soff + (uint32_t)(4 * g) * (uint32_t)p.ld_row_scales), k, byte, true,
+                         hl == 0);
+      } else {
+        const int64_t row = row0 + r, c0 = col0 + 32 * k;
+        const bool valid = interior || (row < p.rows && c0 < p.cols);
+        if (valid) *(u2v*)(cbase + 4 * g * p.ld_row_codes) = u2v{w[0], w[1]};
+        store_row_scales(sbase + 4 * g * p.ld_row_scales, k, byte, wide_scales && full_width, valid && hl == 0);
+      }
     }
   }
   if constexpr (DO_COL) {
@@ -690,6 +713,10 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const int64_t cl = col0 + 64 * wave + n;
     uint8_t* const ccbase = p.col_codes + cl * p.ld_col_codes + row0 / 2 + 8 * hl;
     uint8_t* const csbase = p.col_scales + cl * p.ld_col_scales + row0 / 32;
+    uint8_t* const ccbase_u = uniform_ptr(p.col_codes + col0 * p.ld_col_codes + row0 / 2);
+    uint8_t* const csbase_u = uniform_ptr(p.col_scales + col0 * p.ld_col_scales + row0 / 32);
+    const uint32_t ccoff = (uint32_t)(64 * wave + n) * (uint32_t)p.ld_col_codes + 8 * hl;
+    const uint32_t csoff = (uint32_t)(64 * wave + n) * (uint32_t)p.ld_col_scales;
     const uint64_t cctr0 = (((uint64_t)cl * (uint64_t)p.rows + (uint64_t)row0) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -721,7 +748,14 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       // counter: (cc * rows + row0) / 8 + 2 hl with cc 32 g columns further, and rows % 32 == 0 here
       const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, cctr0 + (uint64_t)(4 * g) * (uint64_t)p.rows, 1u, k0,
                                                          k1, w);
-      if (cc < p.cols) {
+      if constexpr (FAST) {
+        typedef unsigned int u2c __attribute__((ext_vector_type(2)));
+        *(__attribute__((address_space(1))) u2c*)(ccbase_u + (uint64_t)(ccoff + (uint32_t)(32 * g) * (uint32_t)p.ld_col_codes)) =
+            u2c{w[0], w[1]};
+        if (hl == 0)
+          *(__attribute__((address_space(1))) uint8_t*)(csbase_u + (uint64_t)(csoff + (uint32_t)(32 * g) *
+                                                                                   (uint32_t)p.ld_col_scales)) = (uint8_t)byte;
+      } else if (cc < p.cols) {
         *(uint2*)(ccbase + 32 * g * p.ld_col_codes) = uint2{w[0], w[1]};
         if (hl == 0) csbase[32 * g * p.ld_col_scales] = (uint8_t)byte;
       }
@@ -822,9 +856,17 @@ quant_kernel(const QuantParams p) {
 
     if (HAD > 0 && cls <= kClsMfma3) {
       if constexpr (HAD > 0) {
-        if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
-        else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
-        else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+        const bool fast = p.fast_ok && (!DO_ROW || wide_scales) && row0 + kTileRows <= p.rows &&
+                          col0 + kTileCols <= p.cols;
+        if (fast) {
+          if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1, true>(p, buf, t, row0, col0, htab, t2, t3, true);
+          else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2, true>(p, buf, t, row0, col0, htab, t2, t3, true);
+          else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3, true>(p, buf, t, row0, col0, htab, t2, t3, true);
+        } else {
+          if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1, false>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+          else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2, false>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+          else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3, false>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+        }
       }
     } else {
       // ---- 4c. no rotation, float64 butterflies or exact fixed point: each
@@ -866,6 +908,10 @@ hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int r
   p.n_row_tiles = (int32_t)((p.rows + kTileRows - 1) / kTileRows);
   p.n_col_tiles = (int32_t)((p.cols + kTileCols - 1) / kTileCols);
   p.n_row_groups = (p.n_row_tiles + kGroup - 1) / kGroup;
+  // a tile's output lines lie within 32-bit offsets of its first line: up to 32 row-wise lines and 256
+  // column-wise lines of the given pitches
+  p.fast_ok = (!do_row || (p.ld_row_codes < (int64_t(1) << 26) && p.ld_row_scales < (int64_t(1) << 26))) &&
+              (!do_col || (p.ld_col_codes < (int64_t(1) << 23) && p.ld_col_scales < (int64_t(1) << 23)));
   const int64_t regions = (int64_t)p.n_col_tiles * p.n_row_groups;
   // tiles each XCD walks: its regions (every 8th) x 8 row tiles
   const int64_t per_xcd = ((regions + 7) / 8) * kGroup;
