@@ -356,8 +356,41 @@ def measure_quantizer(x, dev, stream):
         gbs = nbytes / (cold * 1e-6) / 1e9
         q[rounding] = {"us_cold": round(cold, 2), "us_hot": round(hot, 2), "GB/s": round(gbs, 1),
                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    return dict(workload="X 8192x4096 bf16, H32 deterministic, E2M1, row- and column-wise outputs from one launch",
-                bytes_per_call=nbytes, **q)
+    out = dict(workload="X 8192x4096 bf16, H32 deterministic, E2M1, row- and column-wise outputs from one launch",
+               bytes_per_call=nbytes, **q)
+    out["rotation_ablation"] = measure_ablation(xs, sets, stream)
+    return out
+
+
+def measure_ablation(xs, sets, stream):
+    """The rotation's cost, fused and unfused, on the quantizer-only workload (RTNE, both outputs, the same
+    five tensors in rotation): the fused kernel without rotation, with the H32 rotation, and the rotation as
+    its own kernel (float32 y along each axis) followed by the cast of y.  The pages report ~1.06-1.07x for
+    their fused kernels and ~1.4-1.6x unfused, on NVIDIA SM90/SM100 (context, not a target)."""
+    import torch
+    from block_scaled_fp4_hadamard_amd import api
+    n = len(xs)
+    rows, cols = xs[0].shape
+    yr = torch.empty((rows, cols), dtype=torch.float32, device=xs[0].device)
+    yc = torch.empty((cols, rows), dtype=torch.float32, device=xs[0].device)
+
+    def fused(i, had_n):
+        api.quantize(xs[i % n], axis="both", had_n=had_n, had_kind="det", row_out=sets[i % n][0],
+                     col_out=sets[i % n][1])
+
+    def unfused(i):
+        api.hadamard_rotate(xs[i % n], axis="row", had_n=32, out=yr)
+        api.hadamard_rotate(xs[i % n], axis="col", had_n=32, out=yc)
+        api.quantize_f32(yr, axis="row", out=sets[i % n][0])
+        api.quantize_f32(yc, axis="col", out=sets[i % n][1])
+    unfused(0)
+    t_plain = time_us(lambda i: fused(i, 0), 30, stream)
+    t_fused = time_us(lambda i: fused(i, 32), 30, stream)
+    t_unfused = time_us(unfused, 30, stream)
+    return {"us_unrotated": round(t_plain, 2), "us_fused_h32": round(t_fused, 2),
+            "us_unfused_h32": round(t_unfused, 2), "fused_ratio": round(t_fused / t_plain, 3),
+            "unfused_ratio": round(t_unfused / t_plain, 3),
+            "pages_context": "fused ~1.06-1.07x, unfused ~1.4-1.6x on NVIDIA SM90/SM100"}
 
 
 def main():

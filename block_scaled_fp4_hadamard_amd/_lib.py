@@ -17,7 +17,7 @@ HAD = {"none": 0, "det": 1, "rand": 2}
 OUT = {"f32": 0, "bf16": 1}
 
 EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_mxnorm_quantize", "mx_quant_stats",
-           "mx_nvfp4_quantize", "mx_status_str", "mx_version")
+           "mx_nvfp4_quantize", "mx_hadamard_rotate", "mx_quantize_f32", "mx_status_str", "mx_version")
 
 
 class MXError(RuntimeError):
@@ -62,6 +62,10 @@ def lib():
         np_ = ctypes.POINTER(NVTensorC)
         L.mx_nvfp4_quantize.argtypes = [vp, i64, i64, i64, i32, i32, u64, np_, np_, vp]
         L.mx_nvfp4_quantize.restype = ctypes.c_int
+        L.mx_hadamard_rotate.argtypes = [vp, i64, i64, i64, i32, i32, u64, i32, vp, i64, vp]
+        L.mx_hadamard_rotate.restype = ctypes.c_int
+        L.mx_quantize_f32.argtypes = [vp, i64, i64, i64, i32, i32, i32, u64, qp, vp]
+        L.mx_quantize_f32.restype = ctypes.c_int
         L.mx_status_str.argtypes = [ctypes.c_int]
         L.mx_status_str.restype = ctypes.c_char_p
         L.mx_version.argtypes = []
@@ -118,3 +122,11 @@ def mx_nvfp4_quantize(x_ptr, rows, cols, ld_x, rnd, axis, seed, row_q, col_q, st
     return lib().mx_nvfp4_quantize(x_ptr, rows, cols, ld_x, rnd, axis, seed,
                                    ctypes.byref(row_q) if row_q is not None else None,
                                    ctypes.byref(col_q) if col_q is not None else None, stream)
+
+
+def mx_hadamard_rotate(x_ptr, rows, cols, ld_x, had_n, had_kind, had_seed, axis, y_ptr, ld_y, stream):
+    return lib().mx_hadamard_rotate(x_ptr, rows, cols, ld_x, had_n, had_kind, had_seed, axis, y_ptr, ld_y, stream)
+
+
+def mx_quantize_f32(y_ptr, lines, length, ld_y, grid, rnd, axis, seed, out_q, stream):
+    return lib().mx_quantize_f32(y_ptr, lines, length, ld_y, grid, rnd, axis, seed, ctypes.byref(out_q), stream)

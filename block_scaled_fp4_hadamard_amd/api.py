@@ -162,6 +162,36 @@ def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0
             "blocks": int(counts[8])}
 
 
+def hadamard_rotate(x, axis="row", had_n=32, had_kind="det", had_seed=0, out=None):
+    """The block Hadamard rotation alone: a float32 CUDA tensor, (rows, cols) for axis "row" (rotated along
+    rows), or the transpose (cols, rows) for axis "col" (rotated along columns)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    xb = _bits_view(x)
+    rows, cols = x.shape
+    shape = (rows, cols) if axis == "row" else (cols, rows)
+    y = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    if tuple(y.shape) != shape or y.dtype != torch.float32 or y.stride(1) != 1:
+        raise ValueError("out must be a float32 %s tensor with unit column stride" % (shape,))
+    st = _lib.mx_hadamard_rotate(xb.data_ptr(), rows, cols, xb.stride(0), had_n, _lib.HAD[had_kind], had_seed,
+                                 _lib.AXIS[axis], y.data_ptr(), y.stride(0), _stream(x.device))
+    _lib.check(st, "mx_hadamard_rotate")
+    return y
+
+
+def quantize_f32(y, axis="row", grid="e2m1", rounding="rtne", seed=0, out=None):
+    """The MX cast of the lines of a float32 CUDA tensor y (lines, len); axis names which output of the original
+    tensor the lines are ("col": y holds its transpose), which selects the stochastic-rounding stream."""
+    if y.dim() != 2 or y.stride(1) != 1 or y.dtype != torch.float32:
+        raise ValueError("y must be a 2-D float32 tensor with unit column stride")
+    lines, length = y.shape
+    q = out if out is not None else empty_qtensor(lines, length, y.device, grid)
+    st = _lib.mx_quantize_f32(y.data_ptr(), lines, length, y.stride(0), _lib.GRID[grid], _lib.ROUND[rounding],
+                              _lib.AXIS[axis], seed, q.c_struct(), _stream(y.device))
+    _lib.check(st, "mx_quantize_f32")
+    return q
+
+
 @dataclass
 class NVTensor:
     """An NVFP4-style double-block operand: L lines of length K.

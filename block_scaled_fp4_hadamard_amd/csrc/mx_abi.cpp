@@ -280,6 +280,63 @@ mx_status mx_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64
   return MX_OK;
 }
 
+mx_status mx_hadamard_rotate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t had_n,
+                             mx_had had_kind, uint64_t had_seed, mx_axis axis, float* y, int64_t ld_y,
+                             void* hip_stream) {
+  if (rows < 0 || cols < 0) return MX_ERR_INVALID;
+  if (had_kind != MX_HAD_DET && had_kind != MX_HAD_RAND) return MX_ERR_INVALID;
+  if (had_n != 16 && had_n != 32) return MX_ERR_INVALID;
+  if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL) return MX_ERR_INVALID;
+  if (rows == 0 || cols == 0) return MX_OK;
+  const bool col = axis == MX_AXIS_COL;
+  const int64_t len = col ? rows : cols;
+  if (len % 32 != 0) return MX_ERR_INVALID;
+  if (x == nullptr || ((uintptr_t)x & 1u) != 0 || ld_x < cols) return MX_ERR_INVALID;
+  if (y == nullptr || !aligned16(y) || ld_y < len || ld_y % 4 != 0) return MX_ERR_INVALID;
+  mx::RotateParams p{};
+  p.x = x;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld_x = ld_x;
+  p.y = y;
+  p.ld_y = ld_y;
+  p.col = col;
+  p.sign_mask = 0u;
+  const bool rht = had_kind == MX_HAD_RAND;
+  if (rht) {
+    const uint32_t w0 = philox_word0(0u, 0u, 2u, 0u, (uint32_t)had_seed, (uint32_t)(had_seed >> 32));
+    p.sign_mask = had_n == 32 ? w0 : (w0 & 0xFFFFu);
+  }
+  hipError_t e = mx::launch_rotate(p, had_n, rht, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
+mx_status mx_quantize_f32(const float* y, int64_t lines, int64_t len, int64_t ld_y, mx_grid grid, mx_round round,
+                          mx_axis axis, uint64_t seed, const mx_qtensor* out, void* hip_stream) {
+  if (lines < 0 || len < 0) return MX_ERR_INVALID;
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (round != MX_ROUND_RTNE && round != MX_ROUND_SR) return MX_ERR_INVALID;
+  if (axis != MX_AXIS_ROW && axis != MX_AXIS_COL) return MX_ERR_INVALID;
+  if (lines == 0 || len == 0) return MX_OK;
+  if (len % 32 != 0) return MX_ERR_INVALID;
+  if (y == nullptr || !aligned16(y) || ld_y < len || ld_y % 4 != 0) return MX_ERR_INVALID;
+  mx_status s = check_qtensor(out, lines, len, 32);
+  if (s != MX_OK) return s;
+  mx::QuantF32Params p{};
+  p.y = y;
+  p.lines = lines;
+  p.len = len;
+  p.ld_y = ld_y;
+  p.codes = out->codes;
+  p.ld_codes = out->ld_codes;
+  p.scales = out->scales;
+  p.ld_scales = out->ld_scales;
+  p.seed = seed;
+  p.stream = axis == MX_AXIS_COL ? 1u : 0u;
+  hipError_t e = mx::launch_quant_f32(p, grid, round, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
 const char* mx_status_str(mx_status status) {
   switch (status) {
     case MX_OK: return "MX_OK";

@@ -26,6 +26,33 @@ struct QuantParams {
 hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int round, bool do_row, bool do_col,
                         hipStream_t s);
 
+// The rotation alone: float32 y of every 32-value block along one axis
+// (column axis: y holds the transpose, y[c][r]).
+struct RotateParams {
+  const uint16_t* x;
+  int64_t rows, cols, ld_x;
+  float* y;
+  int64_t ld_y;         // floats between lines of y
+  bool col;
+  uint32_t sign_mask;   // bit j set: input j of every Hadamard chunk is negated
+};
+
+hipError_t launch_rotate(RotateParams p, int had_n, bool rht, hipStream_t s);
+
+// The MX cast of float32 lines (block 32), stochastic-rounding stream `stream`.
+struct QuantF32Params {
+  const float* y;
+  int64_t lines, len, ld_y;
+  uint8_t* codes;
+  int64_t ld_codes;
+  uint8_t* scales;
+  int64_t ld_scales;
+  uint64_t seed;
+  uint32_t stream;
+};
+
+hipError_t launch_quant_f32(const QuantF32Params& p, int grid_kind, int round, hipStream_t s);
+
 struct GemmParams {
   const uint8_t* a_codes;
   const uint8_t* a_scales;

@@ -928,3 +928,109 @@ hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int r
 }
 
 }  // namespace mx
+
+// ---------------------------------------------------------------------------
+// The unfused path: the rotation alone, writing float32 y, and the MX cast of
+// float32 lines ("Ripensare il Bias di Shrinkage ...", Efficienza: the random
+// Hadamard transform fused with the FP4 quantization against the two run
+// apart).  Rotating, then casting, gives the fused kernel's codes and scales
+// bit for bit: y is the same RN32(RN32(S) * c) of the exact sum S.
+namespace mx {
+
+// One thread per 32-value block along the rotation axis.  Row axis: block k
+// of row r, y[r][32k ..]; column axis: block k of column c (rows 32k ..),
+// stored transposed, y[c][32k ..].  Adjacent threads take adjacent blocks of a
+// row, or adjacent columns, so loads are contiguous across a wave.  Blocks the
+// float64 butterflies could get wrong (more than 40 binades, non-finite or
+// near-overflow inputs) are computed exactly, one output at a time.
+template <int HAD>
+__global__ void __launch_bounds__(kThreads) rotate_kernel(const RotateParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t nblk = p.col ? p.rows / 32 : p.cols / 32;
+  const int64_t lines = p.col ? p.cols : p.rows;
+  if (idx >= lines * nblk) return;
+  int64_t line, k;
+  if (p.col) {
+    line = idx % p.cols;
+    k = idx / p.cols;
+  } else {
+    line = idx / nblk;
+    k = idx % nblk;
+  }
+  const uint16_t* src = p.col ? p.x + (32 * k) * p.ld_x + line : p.x + line * p.ld_x + 32 * k;
+  const int64_t step = p.col ? p.ld_x : 1;
+  auto get = [&](int j) { return (uint32_t)src[j * step]; };
+  float y[32];
+  if (block_needs_exact<HAD>(get)) {
+#pragma unroll 1
+    for (int i = 0; i < 32; ++i) y[i] = special_value<HAD>(get, i, p.sign_mask);
+  } else {
+    load_rotate<HAD>(
+        [&](int h, float (&x)[16]) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = __uint_as_float(get(16 * h + i) << 16);
+        },
+        p.sign_mask, y);
+  }
+  float4* dst = (float4*)(p.y + line * p.ld_y + 32 * k);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[i] = float4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+}
+
+// One thread per 32-value block of a float32 line: block absmax, E8M0 scale,
+// cast, as the fused kernel's cast of the same y (stochastic-rounding element
+// index line * len + j in `stream`).  A block holding a non-finite value gets
+// scale 0xFF and zero codes.
+template <int GRID, int ROUND>
+__global__ void __launch_bounds__(kThreads) quant_f32_kernel(const QuantF32Params p) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t nblk = p.len / 32;
+  if (idx >= p.lines * nblk) return;
+  const int64_t line = idx / nblk, k = idx % nblk;
+  const float4* src = (const float4*)(p.y + line * p.ld_y + 32 * k);
+  float y[32];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = src[i];
+    y[4 * i] = v.x;
+    y[4 * i + 1] = v.y;
+    y[4 * i + 2] = v.z;
+    y[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mx = max(mx, __float_as_uint(y[i]) & 0x7FFFFFFFu);
+  uint32_t w[4];
+  uint32_t byte = cast_block<GRID, ROUND>(y, (uint64_t)(line * p.len + 32 * k) >> 3, p.stream, (uint32_t)p.seed,
+                                          (uint32_t)(p.seed >> 32), w);
+  if (mx >= 0x7F800000u) {
+    byte = 0xFFu;
+    w[0] = w[1] = w[2] = w[3] = 0u;
+  }
+  *(uint4*)(p.codes + line * p.ld_codes + 16 * k) = uint4{w[0], w[1], w[2], w[3]};
+  p.scales[line * p.ld_scales + k] = (uint8_t)byte;
+}
+
+hipError_t launch_rotate(RotateParams p, int had_n, bool rht, hipStream_t s) {
+  if (!rht) p.sign_mask = 0u;
+  const int64_t blocks = p.rows * p.cols / 32;
+  const dim3 g((unsigned)((blocks + kThreads - 1) / kThreads));
+  if (had_n == 16) hipLaunchKernelGGL(rotate_kernel<16>, g, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL(rotate_kernel<32>, g, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_f32(const QuantF32Params& p, int grid_kind, int round, hipStream_t s) {
+  const int64_t blocks = p.lines * (p.len / 32);
+  const dim3 g((unsigned)((blocks + kThreads - 1) / kThreads));
+  if (grid_kind == MX_GRID_E2M1) {
+    if (round == MX_ROUND_RTNE) hipLaunchKernelGGL((quant_f32_kernel<MX_GRID_E2M1, MX_ROUND_RTNE>), g, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((quant_f32_kernel<MX_GRID_E2M1, MX_ROUND_SR>), g, dim3(kThreads), 0, s, p);
+  } else {
+    if (round == MX_ROUND_RTNE) hipLaunchKernelGGL((quant_f32_kernel<MX_GRID_E1M2, MX_ROUND_RTNE>), g, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((quant_f32_kernel<MX_GRID_E1M2, MX_ROUND_SR>), g, dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mx

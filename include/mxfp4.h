@@ -250,6 +250,43 @@ mx_status mx_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
                             mx_axis axis, uint64_t seed, const mx_nvfp4_tensor *row_out,
                             const mx_nvfp4_tensor *col_out, void *hip_stream);
 
+/*
+ * mx_hadamard_rotate: the block Hadamard rotation alone, as float32 ("Ripensare
+ * il Bias di Shrinkage nel Pretraining di LLM in FP4", Efficienza: the random
+ * Hadamard transform fused with the FP4 quantization against the two run as
+ * separate kernels; this and mx_quantize_f32 are the separate kernels).
+ * y = RN32(RN32(S) * RN32(1/sqrt(n))) of the exact sum, as for
+ * mx_hadamard_quantize, for every aligned chunk of had_n values along the axis.
+ *   x, rows, cols, ld_x  device bf16 bit patterns (2-byte aligned, ld_x >= cols)
+ *   had_n, had_kind, had_seed  as mx_hadamard_quantize (MX_HAD_DET or MX_HAD_RAND)
+ *   axis       MX_AXIS_ROW: rotate along each row; y is [rows][ld_y], cols % 32 == 0
+ *              MX_AXIS_COL: rotate along each column; y holds the transpose,
+ *              [cols][ld_y] with y[c][r], rows % 32 == 0
+ *   y, ld_y    device float32, 16-byte aligned; ld_y (floats) >= the rotated
+ *              axis' length and a multiple of 4
+ */
+mx_status mx_hadamard_rotate(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, int32_t had_n,
+                             mx_had had_kind, uint64_t had_seed, mx_axis axis, float *y, int64_t ld_y,
+                             void *hip_stream);
+
+/*
+ * mx_quantize_f32: the MX cast (block 32) of float32 lines, as mx_quantize
+ * casts the values it computes: block absmax, E8M0 scale, RTNE or stochastic
+ * rounding, a block holding a non-finite value getting scale 0xFF and codes 0.
+ * With y from mx_hadamard_rotate the codes and scales equal those of
+ * mx_hadamard_quantize for the same axis.
+ *   y          device float32 [lines][ld_y], 16-byte aligned, ld_y >= len and a
+ *              multiple of 4; len % 32 == 0
+ *   axis       which output of the original tensor the lines are, for the
+ *              stochastic-rounding draws: MX_AXIS_ROW (its rows, stream 0) or
+ *              MX_AXIS_COL (its columns, y holding the transpose, stream 1);
+ *              element j of line l has index l * len + j
+ *   grid, round, seed   as mx_quantize
+ *   out        lines lines of length len (codes 16-byte aligned)
+ */
+mx_status mx_quantize_f32(const float *y, int64_t lines, int64_t len, int64_t ld_y, mx_grid grid, mx_round round,
+                          mx_axis axis, uint64_t seed, const mx_qtensor *out, void *hip_stream);
+
 /* A static, human-readable name for a status code. */
 const char *mx_status_str(mx_status status);
 

@@ -178,3 +178,33 @@ def test_binding_passes_the_operand_block_size():
         api.gemm(bad, bad)
     with pytest.raises(ValueError):
         api.quantize(torch.zeros((32, 512), dtype=torch.bfloat16), row_out=a16)    # block 32 into a 16 operand
+
+
+def rot(x=FAKE, rows=64, cols=128, ld=128, had_n=32, kind=1, axis=1, y=FAKE, ldy=128):
+    return _lib.mx_hadamard_rotate(x, rows, cols, ld, had_n, kind, 0, axis, y, ldy, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), 1), (dict(had_n=8), 1), (dict(kind=0), 1), (dict(kind=3), 1), (dict(axis=3), 1),
+    (dict(axis=0), 1), (dict(cols=120, ld=128), 1), (dict(rows=40, axis=2, ldy=40), 1), (dict(x=0), 1),
+    (dict(x=FAKE + 1), 1), (dict(ld=100), 1), (dict(y=0), 1), (dict(y=FAKE + 8), 1), (dict(ldy=100), 1),
+    (dict(ldy=130), 1), (dict(rows=0), 0), (dict(cols=0), 0),
+])
+def test_rotate_validation(kw, want):
+    assert rot(**kw) == want
+
+
+def qf32(y=FAKE, lines=64, length=128, ldy=128, grid=0, rnd=0, axis=1, out="d"):
+    out = q() if out == "d" else out
+    if out is None:
+        return _lib.lib().mx_quantize_f32(y, lines, length, ldy, grid, rnd, axis, 0, None, None)
+    return _lib.mx_quantize_f32(y, lines, length, ldy, grid, rnd, axis, 0, out, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(lines=-1), 1), (dict(grid=2), 1), (dict(rnd=3), 1), (dict(axis=3), 1), (dict(length=120, ldy=120), 1),
+    (dict(y=0), 1), (dict(y=FAKE + 4), 1), (dict(ldy=100), 1), (dict(ldy=130), 1), (dict(out=q(ld_codes=32)), 1),
+    (dict(out=None), 1), (dict(lines=0), 0), (dict(length=0), 0),
+])
+def test_quantize_f32_validation(kw, want):
+    assert qf32(**kw) == want
