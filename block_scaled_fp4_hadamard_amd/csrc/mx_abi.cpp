@@ -291,7 +291,7 @@ mx_status mx_hadamard_rotate(const uint16_t* x, int64_t rows, int64_t cols, int6
   const bool col = axis == MX_AXIS_COL;
   const int64_t len = col ? rows : cols;
   if (len % 32 != 0) return MX_ERR_INVALID;
-  if (x == nullptr || ((uintptr_t)x & 1u) != 0 || ld_x < cols) return MX_ERR_INVALID;
+  if (x == nullptr || !aligned16(x) || ld_x < cols || ld_x % 8 != 0 || cols % 8 != 0) return MX_ERR_INVALID;
   if (y == nullptr || !aligned16(y) || ld_y < len || ld_y % 4 != 0) return MX_ERR_INVALID;
   mx::RotateParams p{};
   p.x = x;

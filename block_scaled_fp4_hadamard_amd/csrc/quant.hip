@@ -937,29 +937,33 @@ hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int r
 // bit for bit: y is the same RN32(RN32(S) * c) of the exact sum S.
 namespace mx {
 
-// One thread per 32-value block along the rotation axis.  Row axis: block k
-// of row r, y[r][32k ..]; column axis: block k of column c (rows 32k ..),
-// stored transposed, y[c][32k ..].  Adjacent threads take adjacent blocks of a
-// row, or adjacent columns, so loads are contiguous across a wave.  Blocks the
-// float64 butterflies could get wrong (more than 40 binades, non-finite or
-// near-overflow inputs) are computed exactly, one output at a time.
+// A workgroup takes a 32-row x 256-column tile.  The bf16 tile is read with
+// coalesced 16-byte loads into LDS; thread t then rotates one 32-value block
+// (row axis: block t % 8 of tile row t / 8; column axis: tile column t) from
+// LDS and writes its 32 results into an LDS tile of y, which the workgroup
+// stores with coalesced 16-byte stores: whole 128-byte lines of y[r][...] (row
+// axis) or of the transposed y[c][...] (column axis).  Blocks the float64
+// butterflies could get wrong (more than 40 binades, non-finite or
+// near-overflow inputs) are computed exactly, one output at a time.  Edge
+// tiles of a ragged tensor store only what lies inside it.
 template <int HAD>
 __global__ void __launch_bounds__(kThreads) rotate_kernel(const RotateParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t nblk = p.col ? p.rows / 32 : p.cols / 32;
-  const int64_t lines = p.col ? p.cols : p.rows;
-  if (idx >= lines * nblk) return;
-  int64_t line, k;
-  if (p.col) {
-    line = idx % p.cols;
-    k = idx / p.cols;
-  } else {
-    line = idx / nblk;
-    k = idx % nblk;
+  __shared__ __attribute__((aligned(16))) uint16_t xt[kTileRows][kTileCols];     // 16 KB of bf16
+  __shared__ __attribute__((aligned(16))) float yt[kTileRows * kTileCols];       // 32 KB of results
+  const int t = threadIdx.x;
+  const int64_t tiles_c = (p.cols + kTileCols - 1) / kTileCols;
+  const int64_t row0 = (int64_t)(blockIdx.x / tiles_c) * kTileRows, col0 = (int64_t)(blockIdx.x % tiles_c) * kTileCols;
+  // load: piece i = t + 256 q (q = 0..3) is 8 values of row i / 32 at column 8 (i % 32)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = t + kThreads * q, r = i >> 5, c = 8 * (i & 31);
+    uint4 v = uint4{0u, 0u, 0u, 0u};
+    if (row0 + r < p.rows && col0 + c < p.cols) v = *(const uint4*)(p.x + (row0 + r) * p.ld_x + col0 + c);
+    *(uint4*)&xt[r][c] = v;
   }
-  const uint16_t* src = p.col ? p.x + (32 * k) * p.ld_x + line : p.x + line * p.ld_x + 32 * k;
-  const int64_t step = p.col ? p.ld_x : 1;
-  auto get = [&](int j) { return (uint32_t)src[j * step]; };
+  __syncthreads();
+  const int lr = p.col ? 0 : t >> 3, lc = p.col ? t : 32 * (t & 7);
+  auto get = [&](int j) { return (uint32_t)(p.col ? xt[j][lc] : xt[lr][lc + j]); };
   float y[32];
   if (block_needs_exact<HAD>(get)) {
 #pragma unroll 1
@@ -972,9 +976,23 @@ __global__ void __launch_bounds__(kThreads) rotate_kernel(const RotateParams p) 
         },
         p.sign_mask, y);
   }
-  float4* dst = (float4*)(p.y + line * p.ld_y + 32 * k);
+  // thread t's 32 results are line t / 8, values 32 (t % 8) .. of the row-axis tile (32 lines of 256), or
+  // line t of the column-axis tile (256 lines of 32); either way 128 contiguous bytes, block t of yt.  Its
+  // 16-byte piece s sits at slot (s + t) % 8 of the block, so that a wave's writes spread over the banks.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i] = float4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+  for (int i = 0; i < 8; ++i)
+    *(float4*)&yt[32 * t + 4 * ((i + t) & 7)] = float4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+  __syncthreads();
+  // store: piece i = t + 256 q of the 2048 16-byte pieces, piece i % 8 of block i / 8; row axis: tile row
+  // i / 64, columns 4 (i % 64); column axis: tile column i / 8, rows 4 (i % 8)
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = t + kThreads * q, b = i >> 3;
+    const int64_t line = p.col ? col0 + b : row0 + (i >> 6);
+    const int64_t pos = p.col ? row0 + 4 * (i & 7) : col0 + 4 * (i & 63);
+    const bool inside = p.col ? (line < p.cols && pos < p.rows) : (line < p.rows && pos < p.cols);
+    if (inside) *(float4*)(p.y + line * p.ld_y + pos) = *(const float4*)&yt[32 * b + 4 * ((i + b) & 7)];
+  }
 }
 
 // One thread per 32-value block of a float32 line: block absmax, E8M0 scale,
@@ -1013,8 +1031,8 @@ __global__ void __launch_bounds__(kThreads) quant_f32_kernel(const QuantF32Param
 
 hipError_t launch_rotate(RotateParams p, int had_n, bool rht, hipStream_t s) {
   if (!rht) p.sign_mask = 0u;
-  const int64_t blocks = p.rows * p.cols / 32;
-  const dim3 g((unsigned)((blocks + kThreads - 1) / kThreads));
+  const int64_t tiles = ((p.rows + kTileRows - 1) / kTileRows) * ((p.cols + kTileCols - 1) / kTileCols);
+  const dim3 g((unsigned)tiles);
   if (had_n == 16) hipLaunchKernelGGL(rotate_kernel<16>, g, dim3(kThreads), 0, s, p);
   else hipLaunchKernelGGL(rotate_kernel<32>, g, dim3(kThreads), 0, s, p);
   return hipGetLastError();

@@ -257,7 +257,8 @@ mx_status mx_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64
  * separate kernels; this and mx_quantize_f32 are the separate kernels).
  * y = RN32(RN32(S) * RN32(1/sqrt(n))) of the exact sum, as for
  * mx_hadamard_quantize, for every aligned chunk of had_n values along the axis.
- *   x, rows, cols, ld_x  device bf16 bit patterns (2-byte aligned, ld_x >= cols)
+ *   x, rows, cols, ld_x  device bf16 bit patterns, 16-byte aligned; ld_x >= cols,
+ *              ld_x % 8 == 0, cols % 8 == 0
  *   had_n, had_kind, had_seed  as mx_hadamard_quantize (MX_HAD_DET or MX_HAD_RAND)
  *   axis       MX_AXIS_ROW: rotate along each row; y is [rows][ld_y], cols % 32 == 0
  *              MX_AXIS_COL: rotate along each column; y holds the transpose,

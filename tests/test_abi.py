@@ -187,8 +187,9 @@ def rot(x=FAKE, rows=64, cols=128, ld=128, had_n=32, kind=1, axis=1, y=FAKE, ldy
 @pytest.mark.parametrize("kw,want", [
     (dict(rows=-1), 1), (dict(had_n=8), 1), (dict(kind=0), 1), (dict(kind=3), 1), (dict(axis=3), 1),
     (dict(axis=0), 1), (dict(cols=120, ld=128), 1), (dict(rows=40, axis=2, ldy=40), 1), (dict(x=0), 1),
-    (dict(x=FAKE + 1), 1), (dict(ld=100), 1), (dict(y=0), 1), (dict(y=FAKE + 8), 1), (dict(ldy=100), 1),
-    (dict(ldy=130), 1), (dict(rows=0), 0), (dict(cols=0), 0),
+    (dict(x=FAKE + 1), 1), (dict(x=FAKE + 8), 1), (dict(ld=100), 1), (dict(ld=132), 1), (dict(y=0), 1),
+    (dict(y=FAKE + 8), 1), (dict(ldy=100), 1), (dict(ldy=130), 1), (dict(rows=64, cols=36, ld=40, axis=2), 1),
+    (dict(rows=0), 0), (dict(cols=0), 0),
 ])
 def test_rotate_validation(kw, want):
     assert rot(**kw) == want
