@@ -14,6 +14,7 @@ It is plain, slow and written to be checked by eye against the pages:
   quantize  - rotate, block absmax, scale, RTNE/SR cast, pack
   gemm      - decode and the float64 GEMM with its tolerance scale
   recipe    - which operand is quantized along which axis for the three GEMMs
+  osci_reset - oscillation tracking and reset of master weights (TetraJet-v2's OsciReset)
 Every part is pinned by the CPU tests against closed forms, brute force or an
 independent construction (scipy's Hadamard, torch's Philox header).
 """
