@@ -286,7 +286,7 @@ def gemm_entry(us, m, n, k, what):
             "frac_mfma": round(tf / FP4_PEAK_TFLOPS, 4)}
 
 
-WORKLOADS = ("quantizer", "fprop_qkv", "mlp_dgrad", "mlp_wgrad")
+WORKLOADS = ("quantizer", "fprop_qkv", "mlp_dgrad", "mlp_wgrad", "osci_reset")
 
 
 def measure_configs(dev, stream, only=None):
@@ -327,6 +327,8 @@ def measure_configs(dev, stream, only=None):
         us = time_us(lambda i: api.gemm(qdr, qw, out=dx), 20, stream)
         out["mlp_dgrad"] = gemm_entry(us, 8192, 4096, 14336, "dX = dY W_down (shapes as printed), RTNE, bf16 out")
         del qdr, qw, dx
+    if "osci_reset" in want and only:
+        out["osci_reset"] = measure_osci(dev, stream)
     if "mlp_wgrad" in want:
         qd = api.quantize(gpu(d["dy"]), axis="col", rounding="sr", seed=4000)["col"]
         qx = api.quantize(gpu(d["x"]), axis="col", rounding="sr", seed=4002)["col"]
@@ -391,6 +393,29 @@ def measure_ablation(xs, sets, stream):
             "us_unfused_h32": round(t_unfused, 2), "fused_ratio": round(t_fused / t_plain, 3),
             "unfused_ratio": round(t_unfused / t_plain, 3),
             "pages_context": "fused ~1.06-1.07x, unfused ~1.4-1.6x on NVIDIA SM90/SM100"}
+
+
+def measure_osci(dev, stream, rows=14336, cols=4096):
+    """OsciReset on one float32 master weight of the block's largest shape (14336 x 4096), tracking steps and a
+    check, with the weight's row-wise E2M1 quantization as input.  Algorithmic bytes per element of a tracking
+    step: the weight, its code and scale, and the four state arrays read (4 + 0.5 + 1/32 + 16), the four state
+    arrays written (16)."""
+    import torch
+    from block_scaled_fp4_hadamard_amd import api
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    w = torch.randn((rows, cols), device=dev, generator=g) * 0.02
+    q = api.quantize_f32(w)
+    st = api.OsciState.empty_like(w)
+    api.osci_reset(w, q, st, "init")
+    n = rows * cols
+    nbytes = int(n * (4 + 0.5 + 1 / 32 + 16 + 16))
+    track = time_us(lambda i: api.osci_reset(w, q, st, "track"), 20, stream)
+    check = time_us(lambda i: api.osci_reset(w, q, st, "check", 1e30), 20, stream)
+    gbs = nbytes / (track * 1e-6) / 1e9
+    return {"workload": "OsciReset on a %dx%d float32 master weight (E2M1 row-wise quantization)" % (rows, cols),
+            "bytes_per_track_step": nbytes, "us_track": round(track, 2), "us_check": round(check, 2),
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -459,6 +484,7 @@ def main():
     del step2
     log("%s step: %.3f ms" % (other, ms2))
     configs = measure_configs(dev, stream)
+    configs["osci_reset"] = measure_osci(dev, stream)
     log("workloads timed")
     qms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("quant"))
     gms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("gemm"))

@@ -15,9 +15,11 @@ ROUND = {"rtne": 0, "sr": 1}
 AXIS = {"row": 1, "col": 2, "both": 3}
 HAD = {"none": 0, "det": 1, "rand": 2}
 OUT = {"f32": 0, "bf16": 1}
+OSCI = {"init": 0, "track": 1, "check": 2}
 
 EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_mxnorm_quantize", "mx_quant_stats",
-           "mx_nvfp4_quantize", "mx_hadamard_rotate", "mx_quantize_f32", "mx_status_str", "mx_version")
+           "mx_nvfp4_quantize", "mx_hadamard_rotate", "mx_quantize_f32", "mx_osci_reset", "mx_status_str",
+           "mx_version")
 
 
 class MXError(RuntimeError):
@@ -66,6 +68,8 @@ def lib():
         L.mx_hadamard_rotate.restype = ctypes.c_int
         L.mx_quantize_f32.argtypes = [vp, i64, i64, i64, i32, i32, i32, u64, qp, vp]
         L.mx_quantize_f32.restype = ctypes.c_int
+        L.mx_osci_reset.argtypes = [vp, i64, i64, i64, qp, i32, vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp]
+        L.mx_osci_reset.restype = ctypes.c_int
         L.mx_status_str.argtypes = [ctypes.c_int]
         L.mx_status_str.restype = ctypes.c_char_p
         L.mx_version.argtypes = []
@@ -130,3 +134,9 @@ def mx_hadamard_rotate(x_ptr, rows, cols, ld_x, had_n, had_kind, had_seed, axis,
 
 def mx_quantize_f32(y_ptr, lines, length, ld_y, grid, rnd, axis, seed, out_q, stream):
     return lib().mx_quantize_f32(y_ptr, lines, length, ld_y, grid, rnd, axis, seed, ctypes.byref(out_q), stream)
+
+
+def mx_osci_reset(w_ptr, rows, cols, ld_w, q, grid, w_prev, q_prev, dist_m, dist_q, ld_state, mode, threshold,
+                  resets_ptr, stream):
+    return lib().mx_osci_reset(w_ptr, rows, cols, ld_w, ctypes.byref(q), grid, w_prev, q_prev, dist_m, dist_q,
+                               ld_state, mode, threshold, resets_ptr, stream)

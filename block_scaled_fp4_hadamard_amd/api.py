@@ -193,6 +193,37 @@ def quantize_f32(y, axis="row", grid="e2m1", rounding="rtne", seed=0, out=None):
 
 
 @dataclass
+class OsciState:
+    """OsciReset's per-element state, float32 tensors shaped like the master weights."""
+    w_prev: torch.Tensor
+    q_prev: torch.Tensor
+    dist_m: torch.Tensor
+    dist_q: torch.Tensor
+
+    @staticmethod
+    def empty_like(w):
+        return OsciState(*(torch.empty_like(w) for _ in range(4)))
+
+
+def osci_reset(w, q, state, mode, threshold=0.0, resets=None):
+    """One OsciReset step on float32 master weights w (rows, cols) given q, their row-wise quantization (a
+    QTensor, block 32); mode "init", "track" or "check".  resets: an optional int64 CUDA tensor of one element
+    to which the number of reset elements is added.  w is updated in place."""
+    if w.dim() != 2 or w.stride(1) != 1 or w.dtype != torch.float32:
+        raise ValueError("w must be a 2-D float32 tensor with unit column stride")
+    for t in (state.q_prev, state.dist_m, state.dist_q):
+        if t.stride() != state.w_prev.stride() or t.shape != w.shape:
+            raise ValueError("the state tensors must share w's shape and one row stride")
+    rows, cols = w.shape
+    st = _lib.mx_osci_reset(w.data_ptr(), rows, cols, w.stride(0), q.c_struct(), _lib.GRID[q.grid],
+                            state.w_prev.data_ptr(), state.q_prev.data_ptr(), state.dist_m.data_ptr(),
+                            state.dist_q.data_ptr(), state.w_prev.stride(0), _lib.OSCI[mode], threshold,
+                            resets.data_ptr() if resets is not None else None, _stream(w.device))
+    _lib.check(st, "mx_osci_reset")
+    return w
+
+
+@dataclass
 class NVTensor:
     """An NVFP4-style double-block operand: L lines of length K.
 

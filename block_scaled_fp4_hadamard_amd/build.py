@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["quant.hip", "gemm.hip", "mxnorm.hip", "diag.hip", "nvfp4.hip", "mx_abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "mxnorm.hip", "diag.hip", "nvfp4.hip", "osci.hip", "mx_abi.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]

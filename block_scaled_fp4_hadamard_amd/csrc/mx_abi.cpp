@@ -337,6 +337,43 @@ mx_status mx_quantize_f32(const float* y, int64_t lines, int64_t len, int64_t ld
   return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
 }
 
+mx_status mx_osci_reset(float* w, int64_t rows, int64_t cols, int64_t ld_w, const mx_qtensor* q, mx_grid grid,
+                        float* w_prev, float* q_prev, float* dist_m, float* dist_q, int64_t ld_state,
+                        mx_osci_mode mode, float threshold, uint64_t* resets, void* hip_stream) {
+  if (rows < 0 || cols < 0) return MX_ERR_INVALID;
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (mode != MX_OSCI_INIT && mode != MX_OSCI_TRACK && mode != MX_OSCI_CHECK) return MX_ERR_INVALID;
+  if (mode == MX_OSCI_CHECK && !(threshold >= 0.0f && threshold <= 3.0e38f)) return MX_ERR_INVALID;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (cols % 32 != 0) return MX_ERR_INVALID;
+  const float* arrays[5] = {w, w_prev, q_prev, dist_m, dist_q};
+  for (const float* a : arrays)
+    if (a == nullptr || !aligned16(a)) return MX_ERR_INVALID;
+  if (ld_w < cols || ld_w % 4 != 0 || ld_state < cols || ld_state % 4 != 0) return MX_ERR_INVALID;
+  if (resets != nullptr && ((uintptr_t)resets & 7u) != 0) return MX_ERR_INVALID;
+  mx_status s = check_qtensor(q, rows, cols, 32);
+  if (s != MX_OK) return s;
+  mx::OsciParams p{};
+  p.w = w;
+  p.rows = rows;
+  p.cols = cols;
+  p.ld_w = ld_w;
+  p.codes = q->codes;
+  p.ld_codes = q->ld_codes;
+  p.scales = q->scales;
+  p.ld_scales = q->ld_scales;
+  p.w_prev = w_prev;
+  p.q_prev = q_prev;
+  p.dist_m = dist_m;
+  p.dist_q = dist_q;
+  p.ld_s = ld_state;
+  p.mode = mode;
+  p.threshold = threshold;
+  p.resets = (unsigned long long*)resets;
+  hipError_t e = mx::launch_osci(p, grid, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
 const char* mx_status_str(mx_status status) {
   switch (status) {
     case MX_OK: return "MX_OK";

@@ -53,6 +53,26 @@ struct QuantF32Params {
 
 hipError_t launch_quant_f32(const QuantF32Params& p, int grid_kind, int round, hipStream_t s);
 
+// OsciReset on float32 master weights and their row-wise MX quantization.
+struct OsciParams {
+  float* w;
+  int64_t rows, cols, ld_w;
+  const uint8_t* codes;
+  int64_t ld_codes;
+  const uint8_t* scales;
+  int64_t ld_scales;
+  float* w_prev;
+  float* q_prev;
+  float* dist_m;
+  float* dist_q;
+  int64_t ld_s;          // floats between rows of the four state arrays
+  int mode;              // mx_osci_mode
+  float threshold;
+  unsigned long long* resets;   // optional count of the elements reset (added to)
+};
+
+hipError_t launch_osci(const OsciParams& p, int grid_kind, hipStream_t s);
+
 struct GemmParams {
   const uint8_t* a_codes;
   const uint8_t* a_scales;

@@ -12,7 +12,8 @@
 
 Kernel families: quant.rtne / quant.sr (the quantizer by rounding mode), gemm.bf16 / gemm.f32 (the GEMM by
 output type), mxnorm (the fused MXNorm cast), nvfp4.row / nvfp4.col and mx16.row /
-mx16.col (the 16-value block quantizers by axis), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
+mx16.col (the 16-value block quantizers by axis), rotate and quant.f32 (the unfused rotation and cast),
+osci (OsciReset), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
 reader can tell when the figures no longer describe the code.
 """
 import argparse
@@ -25,7 +26,7 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("quant.hip", "gemm.hip", "mxnorm.hip", "nvfp4.hip", "mx_device.h", "mx_kernels.h")
+KERNEL_SOURCES = ("quant.hip", "gemm.hip", "mxnorm.hip", "nvfp4.hip", "osci.hip", "mx_device.h", "mx_kernels.h")
 
 
 def sources_hash():
@@ -45,6 +46,12 @@ def kernel_family(name):
         return "gemm.bf16" if m.group(2) == "1" else "gemm.f32"
     if "mxnorm_kernel" in name:
         return "mxnorm"
+    if "rotate_kernel" in name:
+        return "rotate"
+    if "quant_f32_kernel" in name:
+        return "quant.f32"
+    if "osci_kernel" in name:
+        return "osci"
     m = re.search(r"block16_kernel<(\d+), (\d+), (\d+), (true|false)>", name)
     if m:
         return "%s.%s" % ("nvfp4" if m.group(1) == "1" else "mx16", "col" if m.group(4) == "true" else "row")

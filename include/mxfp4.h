@@ -81,6 +81,7 @@ typedef enum { MX_ROUND_RTNE = 0, MX_ROUND_SR = 1 } mx_round;
 typedef enum { MX_AXIS_ROW = 1, MX_AXIS_COL = 2, MX_AXIS_BOTH = 3 } mx_axis;   /* bit mask */
 typedef enum { MX_HAD_NONE = 0, MX_HAD_DET = 1, MX_HAD_RAND = 2 } mx_had;
 typedef enum { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_out;
+typedef enum { MX_OSCI_INIT = 0, MX_OSCI_TRACK = 1, MX_OSCI_CHECK = 2 } mx_osci_mode;
 
 /* An NVFP4-style double-block operand (mx_nvfp4_quantize): L lines of length K. */
 typedef struct {
@@ -287,6 +288,35 @@ mx_status mx_hadamard_rotate(const uint16_t *x, int64_t rows, int64_t cols, int6
  */
 mx_status mx_quantize_f32(const float *y, int64_t lines, int64_t len, int64_t ld_y, mx_grid grid, mx_round round,
                           mx_axis axis, uint64_t seed, const mx_qtensor *out, void *hip_stream);
+
+/*
+ * mx_osci_reset: OsciReset on float32 master weights ("Résumé Technique :
+ * TetraJet-v2", 2. Méthodologie, B: the oscillation risk is the distance the
+ * quantized weight travels over the distance the master weight travels; when
+ * the learning rate is small and the risk exceeds a threshold, the master
+ * weight is reset to the centre of its current quantization bin).  Per
+ * element, in float32 with one rounding per operation:
+ *   q      = the decoded value of w's code in q (level times 2^(scale - 127));
+ *   MX_OSCI_INIT:  w_prev = w, q_prev = q, dist_m = dist_q = 0;
+ *   MX_OSCI_TRACK: dist_m += |w - w_prev|, dist_q += |q - q_prev|;
+ *   MX_OSCI_CHECK: as TRACK, then w = q where dist_q > threshold * dist_m
+ *                  (the caller checks when its learning rate is small), and
+ *                  dist_m = dist_q = 0 everywhere (a new window);
+ *   then w_prev = w, q_prev = q.
+ *   w          device float32 [rows][ld_w], 16-byte aligned, ld_w % 4 == 0;
+ *              written only where reset
+ *   q          w's row-wise quantization (block 32: e.g. mx_quantize_f32 of w
+ *              with MX_AXIS_ROW), rows lines of length cols; cols % 32 == 0
+ *   grid       the grid q was cast to
+ *   w_prev, q_prev, dist_m, dist_q   device float32 state [rows][ld_state],
+ *              16-byte aligned, ld_state % 4 == 0; written by every mode
+ *   threshold  finite, >= 0 (read by MX_OSCI_CHECK only)
+ *   resets     optional device counter (8-byte aligned, or NULL): the number
+ *              of elements reset is added to it
+ */
+mx_status mx_osci_reset(float *w, int64_t rows, int64_t cols, int64_t ld_w, const mx_qtensor *q, mx_grid grid,
+                        float *w_prev, float *q_prev, float *dist_m, float *dist_q, int64_t ld_state,
+                        mx_osci_mode mode, float threshold, uint64_t *resets, void *hip_stream);
 
 /* A static, human-readable name for a status code. */
 const char *mx_status_str(mx_status status);

@@ -209,3 +209,21 @@ def qf32(y=FAKE, lines=64, length=128, ldy=128, grid=0, rnd=0, axis=1, out="d"):
 ])
 def test_quantize_f32_validation(kw, want):
     assert qf32(**kw) == want
+
+
+def osci(w=FAKE, rows=64, cols=128, ldw=128, q_="d", grid=0, st=FAKE, lds=128, mode=1, thr=2.0, resets=None):
+    qq = q() if q_ == "d" else q_
+    if qq is None:
+        return _lib.lib().mx_osci_reset(w, rows, cols, ldw, None, grid, st, st, st, st, lds, mode, thr, resets, None)
+    return _lib.mx_osci_reset(w, rows, cols, ldw, qq, grid, st, st, st, st, lds, mode, thr, resets, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(rows=-1), 1), (dict(grid=2), 1), (dict(mode=3), 1), (dict(mode=2, thr=-1.0), 1),
+    (dict(mode=2, thr=float("nan")), 1), (dict(mode=2, thr=float("inf")), 1), (dict(cols=120, ldw=120, lds=120), 1),
+    (dict(w=0), 1), (dict(w=FAKE + 4), 1), (dict(st=0), 1), (dict(st=FAKE + 8), 1), (dict(ldw=100), 1),
+    (dict(ldw=130), 1), (dict(lds=126), 1), (dict(q_=None), 1), (dict(q_=q(ld_codes=32)), 1),
+    (dict(resets=FAKE + 4), 1), (dict(rows=0), 0), (dict(cols=0), 0),
+])
+def test_osci_validation(kw, want):
+    assert osci(**kw) == want
