@@ -12,8 +12,9 @@
 // by op_sel; the 32x32 fp32 result sits in 16 registers, register r of lane l
 // being row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
 //
-// The uniform E1M2 grid runs on the same instruction with 6-bit E2M3
-// operands: code (s, k) maps exactly to (s << 5) | (k << 1), value k/4.
+// The uniform E1M2 grid runs on the same instruction with FP8 E4M3 operands
+// (every value k/4 is exact in E4M3), converted after the LDS read; the
+// FP6 E2M3 form (s << 5) | (k << 1) is kept as the alternative carrier.
 //
 // Tiling: a 256-lane workgroup owns a 256x256 block of C (four waves of
 // 128x128 = 4x4 MFMA tiles), K advances 128 elements (64 bytes per row) per
@@ -58,6 +59,63 @@ __device__ __forceinline__ void e1m2_to_e2m3(const uint32_t (&in)[4], uint32_t (
   out[4] = (uint32_t)(c2 >> 32) | ((uint32_t)c3 << 16);
   out[5] = (uint32_t)(c3 >> 16);
 }
+
+// E1M2 code nibbles (8 per dword) -> FP8 E4M3 bytes with the same values
+// (k/4 for magnitude code k, sign from bit 3): a byte-permute table lookup of
+// the magnitude codes and the sign bit moved to bit 7.  The even nibbles of a
+// dword land in the low output dword and the odd ones in the high one, so a
+// block's values are reordered; both operands are reordered alike and the
+// block's scale is shared, so the dot product is the same sum.
+//
+// The 8-bit operand layout differs from the 4- and 6-bit one: in every lane,
+// bytes 0-15 belong to the first 32-wide block of the 64 k (scaled by lane
+// l % 32's scale) and bytes 16-31 to the second (lane l % 32 + 32's scale).
+// Lane l < 32 converts block 0 and lane l + 32 block 1, so the upper 16 bytes
+// of the low lanes trade places with the lower 16 bytes of the high lanes.
+constexpr uint32_t kE4M3QuarterLo = 0x34302800u;   // 0, 0.25, 0.5, 0.75
+constexpr uint32_t kE4M3QuarterHi = 0x3E3C3A38u;   // 1, 1.25, 1.5, 1.75
+__device__ __forceinline__ void e1m2_to_e4m3(const uint32_t (&in)[4], uint32_t (&out)[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w = in[d];
+    const uint32_t lo = __builtin_amdgcn_perm(kE4M3QuarterHi, kE4M3QuarterLo, w & 0x07070707u);
+    const uint32_t hi = __builtin_amdgcn_perm(kE4M3QuarterHi, kE4M3QuarterLo, (w >> 4) & 0x07070707u);
+    out[2 * d] = lo | ((w << 4) & 0x80808080u);
+    out[2 * d + 1] = hi | (w & 0x80808080u);
+  }
+}
+
+// the FP8 or the FP6 carrier of the uniform grid on the matrix cores
+constexpr bool kE1M2AsFp8 = true;
+
+// One lane's MFMA operand from its 16 code bytes (32 values of a block): E2M1
+// as is (fp4), E1M2 as FP8 E4M3 (exchanged across the wave's halves, so the
+// whole wave must call it together) or FP6 E2M3 of the same values.
+template <int GRID>
+__device__ __forceinline__ v8i operand(const uint4& x) {
+  if constexpr (GRID == MX_GRID_E2M1) {
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  } else if constexpr (kE1M2AsFp8) {
+    uint32_t o8[8];
+    e1m2_to_e4m3({x.x, x.y, x.z, x.w}, o8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // lanes 32-63 of o8[i] <-> lanes 0-31 of o8[4 + i]
+      const auto sw = __builtin_amdgcn_permlane32_swap(o8[i], o8[4 + i], false, false);
+      o8[i] = sw[0];
+      o8[4 + i] = sw[1];
+    }
+    return v8i{(int)o8[0], (int)o8[1], (int)o8[2], (int)o8[3], (int)o8[4], (int)o8[5], (int)o8[6], (int)o8[7]};
+  } else {
+    uint32_t o6[6];
+    e1m2_to_e2m3({x.x, x.y, x.z, x.w}, o6);
+    return v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
+  }
+}
+
+// MFMA format code of a grid's operands: 4 fp4 E2M1; 0 fp8 E4M3 or 2 fp6 E2M3 for E1M2
+template <int GRID>
+constexpr int mfma_fmt() { return GRID == MX_GRID_E2M1 ? 4 : (kE1M2AsFp8 ? 0 : 2); }
 
 // Two floats to packed bf16 (a in the low half) by gfx950's packed conversion:
 // round to nearest even, a NaN quieted with its payload kept.  Over all 2^32
@@ -111,13 +169,7 @@ __device__ __forceinline__ void mma_step(const uint8_t* a, const uint8_t* b, con
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint4 x = *(const uint4*)(a + ar * kBKBytes + swz(ar, 2 * h + half));
-      if constexpr (GRID == MX_GRID_E2M1) {
-        fa[h][i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-      } else {
-        uint32_t o6[6];
-        e1m2_to_e2m3({x.x, x.y, x.z, x.w}, o6);
-        fa[h][i] = v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
-      }
+      fa[h][i] = operand<GRID>(x);
     }
   }
 #pragma unroll
@@ -127,16 +179,10 @@ __device__ __forceinline__ void mma_step(const uint8_t* a, const uint8_t* b, con
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint4 y = *(const uint4*)(b + br * kBKBytes + swz(br, 2 * h + half));
-      if constexpr (GRID == MX_GRID_E2M1) {
-        fb[h][j] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
-      } else {
-        uint32_t o6[6];
-        e1m2_to_e2m3({y.x, y.y, y.z, y.w}, o6);
-        fb[h][j] = v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
-      }
+      fb[h][j] = operand<GRID>(y);
     }
   }
-  constexpr int kFmt = GRID == MX_GRID_E2M1 ? 4 : 2;   // 4: fp4 E2M1, 2: fp6 E2M3
+  constexpr int kFmt = mfma_fmt<GRID>();
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -404,23 +450,13 @@ __device__ __forceinline__ void load_quarter(Frags<NT>& f, const uint8_t* a, con
   }
 }
 
-template <int GRID>
-__device__ __forceinline__ v8i operand(const uint4& x) {
-  if constexpr (GRID == MX_GRID_E2M1) {
-    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-  } else {
-    uint32_t o6[6];
-    e1m2_to_e2m3({x.x, x.y, x.z, x.w}, o6);
-    return v8i{(int)o6[0], (int)o6[1], (int)o6[2], (int)o6[3], (int)o6[4], (int)o6[5], 0, 0};
-  }
-}
 
 // the 8 MFMAs of one quarter; OPSEL picks the scale byte pair (quarters 0,2 -> 0; 1,3 -> 2)
 // Lanes 32-63 hold the odd 32-block of each 64-deep quarter: their scale is
 // one byte above the even block's, so their dwords are shifted by 8.
 template <int GRID, int OPSEL, int NT>
 __device__ __forceinline__ void mfma_quarter(const Frags<NT>& f, v16f (&acc)[4][NT], int shift) {
-  constexpr int kFmt = GRID == MX_GRID_E2M1 ? 4 : 2;   // 4: fp4 E2M1, 2: fp6 E2M3
+  constexpr int kFmt = mfma_fmt<GRID>();
   v8i bj[NT];
   int sbj[NT];
 #pragma unroll
