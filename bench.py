@@ -15,6 +15,8 @@ synthetic tensors of the real shapes, resident in HBM before timing starts.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--unfused]
     python bench.py --calibrate-copy BYTES     (device copies of BYTES, for traffic-counter scaling)
     python bench.py --workloads-only           (only the per-workload timings, for profiler runs)
+    python bench.py --step-only                (only the step's timing, kernels and roofline)
+    python bench.py --mfma-ceiling             (only the probes: FP4 MFMA rate, vector instruction costs)
 
 Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
@@ -22,7 +24,8 @@ with each family's achieved HBM GB/s or MFMA TFLOP/s; `step_e1m2` is the same
 step on the uniform grid; `workloads` times the quantizer-only workload (cold
 and hot, RTNE and SR), the fused-QKV Fprop GEMM and the MLP Dgrad and Wgrad
 GEMMs on their own; `mxnorm` times the fused MXNorm + row-wise cast launch,
-`nvfp4` the double-block quantizer; `roofline` is the dominant kernel's;
+`nvfp4` the double-block quantizer; `mfma_ceiling` the FP4 MFMA's rate on
+register-resident zero, constant and random operands; `roofline` is the dominant kernel's;
 `cpu_baseline` is the CPU oracle on bounded samples.
 """
 import argparse
@@ -38,6 +41,7 @@ if ROOT not in sys.path:
 METRIC = "MXFP4 quantize GB/s (% HBM peak) + FP4 GEMM TFLOPS (% MFMA peak), Llama-3.1-8B"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (the uniform E1M2 grid's GEMMs run on it)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -51,6 +55,11 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     ap.add_argument("--unfused", action="store_true", help="one GEMM per linear instead of fused qkv and gate_up")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only the probes: the FP4 MFMA rate on register-resident zero, constant and random operands, "
+                         "and the issue cost of the cast's vector instructions")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step alone and print its kernels and roofline (for profiler runs)")
     ap.add_argument("--workloads-only", action="store_true",
                     help="time only the quantizer-only, fused-QKV and MLP workloads (for profiler runs)")
     ap.add_argument("--workload", action="append", choices=list(WORKLOADS),
@@ -252,14 +261,19 @@ def time_step(step, steps, stream):
     return ms_per_step, fam
 
 
-def family_table(fam):
+def gemm_peak(grid):
+    """Dense MFMA peak of a grid's GEMMs: E2M1 runs the FP4 MFMA, E1M2 the FP8 one."""
+    return FP4_PEAK_TFLOPS if grid == "e2m1" else FP8_PEAK_TFLOPS
+
+
+def family_table(fam, peak=FP4_PEAK_TFLOPS):
     kernels = {}
     for label, f in fam.items():
         k = {"launches_per_step": f["launches"], "ms_per_step": round(f["ms"], 4),
              "us_per_launch": round(f["ms"] / f["launches"] * 1e3, 2)}
         if f["flops"]:
             k["TFLOP/s"] = round(f["flops"] / (f["ms"] * 1e-3) / 1e12, 1)
-            k["frac_mfma"] = round(k["TFLOP/s"] / FP4_PEAK_TFLOPS, 4)
+            k["frac_mfma"] = round(k["TFLOP/s"] / peak, 4)
         else:
             k["GB/s"] = round(f["bytes"] / (f["ms"] * 1e-3) / 1e9, 1)
             k["frac_hbm"] = round(k["GB/s"] / HBM_PEAK_GBS, 4)
@@ -278,6 +292,75 @@ def time_us(fn, reps, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps * 1e3
+
+
+def mfma_ceiling(dev, stream):
+    """Sustained rate of the block-scaled FP4 MFMA on register-resident operands (libmxprobe.so), launched
+    like the GEMM (256 workgroups x 512 lanes), for zero, constant (every code 1.0) and uniformly random code
+    bytes, all scales 1.0: the ceiling the GEMM's matrix work can reach on this chip at the clock each
+    operand pattern lets it hold."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_scaled_fp4_hadamard_amd", "libmxprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mxp_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.mxp_mfma_rate.restype = ctypes.c_int
+    wgs, threads, iters = 256, 512, 4096
+    n = 256 * 2 * 64 * 16
+    gen = torch.Generator().manual_seed(11)
+    patterns = {"zero": torch.zeros(n, dtype=torch.uint8),
+                "constant": torch.full((n,), 0x22, dtype=torch.uint8),
+                "random": torch.randint(0, 256, (n,), dtype=torch.uint8, generator=gen)}
+    scales = torch.full((256 * 2 * 64,), 127, dtype=torch.int32, device=dev)
+    sink = torch.empty(wgs * threads, dtype=torch.float32, device=dev)
+    flops = wgs * (threads // 64) * iters * 4 * 2.0 * 32 * 32 * 64
+    out = {"launch": "%d workgroups x %d lanes, %d rounds of 4 MFMAs per wave" % (wgs, threads, iters)}
+    for kind, host in patterns.items():
+        frags = host.to(dev)
+        call = lambda i: lib.mxp_mfma_rate(frags.data_ptr(), scales.data_ptr(), iters, wgs, threads,
+                                           sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if call(0) != 0:
+            raise RuntimeError("mxp_mfma_rate rejected its launch")
+        us = time_us(call, 5, stream)
+        tf = flops / (us * 1e-6) / 1e12
+        out[kind] = {"us": round(us, 1), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / FP4_PEAK_TFLOPS, 4)}
+    return out
+
+
+VALU_PROBES = ("v_fma_f32", "v_cvt_scalef32_pk_fp4_f32", "v_cvt_scalef32_sr_pk_fp4_f32",
+               "v_mad_u64_u32 + v_xor_b32", "v_pk_max_u16", "v_mov_b32 DPP + v_add_u32",
+               "v_permlane32_swap_b32 + v_mov_b32 + v_add_u32", "v_mul_lo_u32 + v_add_u32")
+VALU_PROBE_INSTRS = (1, 1, 1, 2, 1, 2, 3, 2)   # instructions per chain and round
+
+
+def valu_rates(dev, stream):
+    """Issue cost of the vector instructions the quantizer's cast uses (libmxprobe.so): nanoseconds per wave
+    instruction and SIMD, and that over v_fma_f32's (1024 workgroups x 256 lanes, 8 chains x 2048 rounds)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_scaled_fp4_hadamard_amd", "libmxprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mxp_valu_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mxp_valu_rate.restype = ctypes.c_int
+    wgs = 1024
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    out = {"launch": "%d workgroups x 256 lanes, 8 independent chains x 2048 rounds per lane" % wgs}
+    base = None
+    for op, name in enumerate(VALU_PROBES):
+        call = lambda i: lib.mxp_valu_rate(op, wgs, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if call(0) != 0:
+            raise RuntimeError("mxp_valu_rate rejected its launch")
+        us = time_us(call, 5, stream)
+        per_simd = wgs * 4 * 2048 * 8 * VALU_PROBE_INSTRS[op] / 1024.0    # wave instructions per SIMD
+        ns = us * 1e3 / per_simd
+        base = base or ns
+        out[name] = {"ns_per_instr_per_simd": round(ns, 3), "vs_fma": round(ns / base, 2)}
+    return out
 
 
 def gemm_entry(us, m, n, k, what):
@@ -435,6 +518,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.mfma_ceiling:
+        st = torch.cuda.current_stream(dev)
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, st), "valu_rates": valu_rates(dev, st)}), flush=True)
+        return 0
     if args.workloads_only:
         print(json.dumps({"workloads": measure_configs(dev, torch.cuda.current_stream(dev), args.workload)}),
               flush=True)
@@ -458,33 +545,40 @@ def main():
     ms_per_step, fam = time_step(step, args.steps, stream)
     wall = time.time() - wall0
     log("timed %d steps: %.3f ms/step (wall %.3f ms/step)" % (args.steps, ms_per_step, wall / args.steps * 1e3))
-    kernels = family_table(fam)
+    peak = gemm_peak(args.grid)
+    kernels = family_table(fam, peak)
     dom = max(fam, key=lambda lb: fam[lb]["ms"])
     f = fam[dom]
     avg_s = f["ms"] / f["launches"] * 1e-3
     traffic = load_traffic(dom)
     if f["flops"]:
         achieved = f["flops"] / f["launches"] / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": dom}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom}
     else:
         achieved = f["bytes"] / f["launches"] / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom}
+    if args.step_only:
+        print(json.dumps({"ms_per_step": round(ms_per_step, 4), "kernels": kernels, "roofline": roof}), flush=True)
+        return 0
     mxnorm = measure_mxnorm(tensors, dev)
     block16 = measure_block16(tensors, dev)
-    # the same step on the other grid (the uniform E1M2 grid's GEMMs run on the FP6 matrix path)
+    # the same step on the other grid (the uniform E1M2 grid's GEMMs run on the FP8 matrix path)
     other = "e1m2" if args.grid == "e2m1" else "e2m1"
     step2 = LlamaBlockStep(tensors, Recipe(grid=other, fuse=not args.unfused))
     step2.run()
     ms2, fam2 = time_step(step2, max(3, args.steps // 2), stream)
     other_step = {"grid": other, "ms_per_step": round(ms2, 4),
                   "value": round(step2.flops / (ms2 * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
-                  "kernels": family_table(fam2)}
+                  "frac_mfma": round(step2.flops / (sum(v["ms"] for lb, v in fam2.items() if lb.startswith("gemm"))
+                                            * 1e-3) / 1e12 / gemm_peak(other), 4),
+                  "kernels": family_table(fam2, gemm_peak(other))}
     del step2
     log("%s step: %.3f ms" % (other, ms2))
     configs = measure_configs(dev, stream)
     configs["osci_reset"] = measure_osci(dev, stream)
+    ceiling = mfma_ceiling(dev, stream)
     log("workloads timed")
     qms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("quant"))
     gms = sum(v["ms"] for lb, v in fam.items() if lb.startswith("gemm"))
@@ -515,13 +609,14 @@ def main():
                    "quant_gb_per_step": round(step.quant_bytes / 1e9, 3)},
         "quantize": {"GB/s": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / HBM_PEAK_GBS, 4),
                      "ms_per_step": round(qms, 4)},
-        "gemm": {"TFLOP/s": round(gemm_tf, 1), "frac_mfma": round(gemm_tf / FP4_PEAK_TFLOPS, 4),
+        "gemm": {"TFLOP/s": round(gemm_tf, 1), "frac_mfma": round(gemm_tf / peak, 4),
                  "ms_per_step": round(gms, 4)},
         "kernels": kernels,
         "step_" + other: other_step,
         "workloads": configs,
         "mxnorm": mxnorm,
         "nvfp4": block16,
+        "mfma_ceiling": ceiling,
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -13,7 +13,7 @@
 Kernel families: quant.rtne / quant.sr (the quantizer by rounding mode), gemm.bf16 / gemm.f32 (the GEMM by
 output type), mxnorm (the fused MXNorm cast), nvfp4.row / nvfp4.col and mx16.row /
 mx16.col (the 16-value block quantizers by axis), rotate and quant.f32 (the unfused rotation and cast),
-osci (OsciReset), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
+osci (OsciReset), probe.mfma and probe.valu (the rate probes), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
 reader can tell when the figures no longer describe the code.
 """
 import argparse
@@ -41,9 +41,9 @@ def kernel_family(name):
     m = re.search(r"quant_kernel<(\d+), (\d+), (\d+),", name)
     if m:
         return "quant.sr" if m.group(3) == "1" else "quant.rtne"
-    m = re.search(r"gemm_\w*kernel<(\d+), (\d+)(, (true|false))?>", name)
-    if m:
-        return "gemm.bf16" if m.group(2) == "1" else "gemm.f32"
+    m = re.search(r"gemm_\w*kernel<(\d+), (\d+)(, [^<>]*)?>", name)
+    if m:   # <grid, output, ...>: the uniform E1M2 grid runs on the FP8 MFMA, a family of its own
+        return "gemm.%s%s" % ("e1m2." if m.group(1) == "1" else "", "bf16" if m.group(2) == "1" else "f32")
     if "mxnorm_kernel" in name:
         return "mxnorm"
     if "rotate_kernel" in name:
@@ -52,6 +52,10 @@ def kernel_family(name):
         return "quant.f32"
     if "osci_kernel" in name:
         return "osci"
+    if "mfma_rate_kernel" in name:
+        return "probe.mfma"
+    if "valu_rate_kernel" in name:
+        return "probe.valu"
     m = re.search(r"block16_kernel<(\d+), (\d+), (\d+), (true|false)>", name)
     if m:
         return "%s.%s" % ("nvfp4" if m.group(1) == "1" else "mx16", "col" if m.group(4) == "true" else "row")

@@ -227,3 +227,22 @@ def osci(w=FAKE, rows=64, cols=128, ldw=128, q_="d", grid=0, st=FAKE, lds=128, m
 ])
 def test_osci_validation(kw, want):
     assert osci(**kw) == want
+
+
+def test_probe_library_exports_and_rejects_bad_launches():
+    """The benchmark's rate probes (libmxprobe.so, not part of the path) load, export their two entry points,
+    and refuse launches outside their bounds before any device work."""
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libmxprobe.so")
+    if not os.path.exists(path):
+        pytest.fail("libmxprobe.so is not built: run python -m block_scaled_fp4_hadamard_amd.build")
+    P = ctypes.CDLL(path)
+    P.mxp_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    P.mxp_valu_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.mxp_mfma_rate(None, FAKE, 1, 1, 64, FAKE, None) == 1
+    assert P.mxp_mfma_rate(FAKE, FAKE, 0, 1, 64, FAKE, None) == 1
+    assert P.mxp_mfma_rate(FAKE, FAKE, 1, 1, 96, FAKE, None) == 1          # not a multiple of 64
+    assert P.mxp_mfma_rate(FAKE, FAKE, 1, 1, 2048, FAKE, None) == 1
+    assert P.mxp_valu_rate(8, 1, FAKE, None) == 1
+    assert P.mxp_valu_rate(0, 0, FAKE, None) == 1
+    assert P.mxp_valu_rate(0, 1, None, None) == 1

@@ -12,8 +12,12 @@ def test_kernel_families():
         "void mx::quant_kernel<32, 0, 0, true, true>(mx::QuantParams)": "quant.rtne",
         "void mx::quant_kernel<32, 0, 1, true, false>(mx::QuantParams)": "quant.sr",
         "void mx::gemm_full_kernel<0, 1, false>(mx::GemmParams, mx::TileMap, int)": "gemm.bf16",
-        "void mx::gemm_full_kernel<1, 0, true>(mx::GemmParams, mx::TileMap, int)": "gemm.f32",
+        "void mx::gemm_full_kernel<1, 0, true>(mx::GemmParams, mx::TileMap, int)": "gemm.e1m2.f32",
         "void mx::gemm_general_kernel<0, 1>(mx::GemmParams, mx::TileMap)": "gemm.bf16",
+        "void mx::gemm_full_kernel<0, 1, false, 2, true>(mx::GemmParams, mx::TileMap, int)": "gemm.bf16",
+        "void mx::gemm_full_kernel<0, 0, true, 2, false>(mx::GemmParams, mx::TileMap, int)": "gemm.f32",
+        "void mx::gemm_full_kernel<1, 1, false, 2, true>(mx::GemmParams, mx::TileMap, int)": "gemm.e1m2.bf16",
+        "void mx::gemm_general_kernel<1, 0>(mx::GemmParams, mx::TileMap)": "gemm.e1m2.f32",
         "void mx::mxnorm_kernel<0, 0, 2>(mx::MxNormParams)": "mxnorm",
         "void mx::block16_kernel<1, 0, 0, true>(mx::Block16Params, long)": "nvfp4.col",
         "void mx::block16_kernel<0, 1, 1, false>(mx::Block16Params, long)": "mx16.row",
