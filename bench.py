@@ -167,72 +167,61 @@ def cpu_baseline(tokens=4096):
     return res
 
 
-def measure_mxnorm(tensors, dev, reps=30):
+def rotation_set(tensors, names):
+    """The named tensors, then copies of them in turn, until more than 1 GiB is in rotation."""
+    xs = [tensors[n] for n in names]
+    need = copies_for(xs[0].numel() * xs[0].element_size())
+    return xs + [xs[i % len(xs)].clone() for i in range(max(0, need - len(xs)))]
+
+
+def measure_mxnorm(tensors, dev, reps=64):
     """The MXNorm + row-wise MX cast launch on the block's 4096-wide tensors, timed apart from the step.
 
-    Six 8192 x 4096 bf16 tensors (403 MB, more than the last-level cache) in rotation, p = 2 with the Monte
-    Carlo constant, E2M1 RTNE; algorithmic bytes per launch: the bf16 read, codes and scales, rho.
+    The block's six 8192 x 4096 bf16 tensors and copies of them, more than 1 GiB in rotation, p = 2 with the
+    Monte Carlo constant, E2M1 RTNE; the median of `reps` launches.  Algorithmic bytes per launch: the bf16
+    read, codes and scales, rho.
     """
     import torch
     from block_scaled_fp4_hadamard_amd import mxnorm_quantize
     from block_scaled_fp4_hadamard_amd.mxnorm_constant import correction
     c = correction(2)
-    names = ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"]
-    xs = [tensors[n] for n in names]
+    xs = rotation_set(tensors, ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"])
     rows, cols = xs[0].shape
     outs = [mxnorm_quantize(x, power=2, c=c) for x in xs]
-    for i, x in enumerate(xs):
-        mxnorm_quantize(x, power=2, c=c, out=outs[i][0], rho=outs[i][1])
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for j in range(reps):
-        i = j % len(xs)
-        mxnorm_quantize(xs[i], power=2, c=c, out=outs[i][0], rho=outs[i][1])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / reps * 1e3
+    us = time_median_us(lambda j: mxnorm_quantize(xs[j % len(xs)], power=2, c=c, out=outs[j % len(xs)][0],
+                                                  rho=outs[j % len(xs)][1]), reps, stream)
     nbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 32 + rows * 4
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": "MXNorm (p=2) fused with the row-wise E2M1 RTNE cast, %dx%d bf16 rows, %d tensors in "
                         "rotation" % (rows, cols, len(xs)),
             "us_per_launch": round(us, 2), "bytes_per_launch": nbytes, "GB/s": round(gbs, 1),
-            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "timing": "median of %d launches" % reps}
 
 
-def measure_block16(tensors, dev, reps=30):
+def measure_block16(tensors, dev, reps=64):
     """The NVFP4-style double-block quantizer (E4M3 per 16 values, float32 per 128), each axis timed apart.
 
-    The same six 8192 x 4096 tensors in rotation, RTNE; algorithmic bytes per launch: the bf16 read, codes,
-    inner and outer scales.
+    The same rotation of more than 1 GiB of 8192 x 4096 tensors, RTNE, the median of `reps` launches;
+    algorithmic bytes per launch: the bf16 read, codes, inner and outer scales.
     """
     import torch
     from block_scaled_fp4_hadamard_amd.api import nvfp4_quantize
-    names = ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"]
-    xs = [tensors[n] for n in names]
+    xs = rotation_set(tensors, ["x_attn", "x_o", "x_mlp", "dy_q", "dy_o", "dy_down"])
     rows, cols = xs[0].shape
     n = rows * cols
     nbytes = 2 * n + n // 2 + n // 16 + 4 * (n // 128)
     res = {"workload": "NVFP4-style double-block E2M1 RTNE cast, %dx%d bf16, %d tensors in rotation, each axis "
-                       "its own launch" % (rows, cols, len(xs)), "bytes_per_launch": nbytes}
+                       "its own launch" % (rows, cols, len(xs)), "bytes_per_launch": nbytes,
+           "timing": "median of %d launches" % reps}
     stream = torch.cuda.current_stream(dev)
     for axis in ("row", "col"):
         outs = [nvfp4_quantize(x, axis=axis)[axis] for x in xs]
         kw = lambda i: {"row_out": outs[i]} if axis == "row" else {"col_out": outs[i]}
-        for i, x in enumerate(xs):
-            nvfp4_quantize(x, axis=axis, **kw(i))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for j in range(reps):
-            i = j % len(xs)
-            nvfp4_quantize(xs[i], axis=axis, **kw(i))
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        us = time_median_us(lambda j: nvfp4_quantize(xs[j % len(xs)], axis=axis, **kw(j % len(xs))), reps, stream)
         gbs = nbytes / (us * 1e-6) / 1e9
         res[axis] = {"us_per_launch": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del outs
     return res
 
 
@@ -279,6 +268,52 @@ def family_table(fam, peak=FP4_PEAK_TFLOPS):
             k["frac_hbm"] = round(k["GB/s"] / HBM_PEAK_GBS, 4)
         kernels[label] = k
     return kernels
+
+
+def time_median_us(fn, reps, stream):
+    """Median microseconds of one call of fn(i), i = 0 .. reps-1, each call bracketed by its own pair of
+    events on the launch stream (the calls still run back to back)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(reps):
+        fn(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(reps))
+    return 1e3 * (t[reps // 2] if reps % 2 else 0.5 * (t[reps // 2 - 1] + t[reps // 2]))
+
+
+COLD_BYTES = 1 << 30      # rotate at least this many input bytes so that no call finds its inputs in the 256 MB
+                          # last-level cache or the L2
+
+
+def copies_for(nbytes):
+    """How many copies of an input of nbytes a cold rotation needs (more than COLD_BYTES in all)."""
+    return max(2, COLD_BYTES // max(1, nbytes) + 1)
+
+
+def clone_qtensor(q):
+    from block_scaled_fp4_hadamard_amd import api
+    c = api.empty_qtensor(q.lines, q.k, q.codes.device, q.grid, q.block)
+    c.codes.copy_(q.codes)
+    c.scales.copy_(q.scales)
+    return c
+
+
+def time_gemm(a, b, out, stream, reps=50):
+    """Median microseconds of the GEMM: cold (operand copies in rotation, more than 1 GiB of operand bytes)
+    and hot (the same operands every call)."""
+    from block_scaled_fp4_hadamard_amd import api
+    nb = sum(t.numel() for t in (a.codes, a.scales, b.codes, b.scales))
+    n = copies_for(nb)
+    ops = [(a, b)] + [(clone_qtensor(a), clone_qtensor(b)) for _ in range(n - 1)]
+    api.gemm(a, b, out=out)
+    cold = time_median_us(lambda i: api.gemm(ops[i % n][0], ops[i % n][1], out=out), reps, stream)
+    hot = time_median_us(lambda i: api.gemm(a, b, out=out), reps, stream)
+    del ops
+    return cold, hot, n
 
 
 def time_us(fn, reps, stream):
@@ -363,10 +398,12 @@ def valu_rates(dev, stream):
     return out
 
 
-def gemm_entry(us, m, n, k, what):
+def gemm_entry(timing, m, n, k, what):
+    us, hot, copies = timing
     tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
     return {"workload": what, "M": m, "N": n, "K": k, "us": round(us, 2), "TFLOP/s": round(tf, 1),
-            "frac_mfma": round(tf / FP4_PEAK_TFLOPS, 4)}
+            "frac_mfma": round(tf / FP4_PEAK_TFLOPS, 4), "us_hot": round(hot, 2),
+            "timing": "median of 50 calls; cold: %d operand copies in rotation" % copies}
 
 
 WORKLOADS = ("quantizer", "fprop_qkv", "mlp_dgrad", "mlp_wgrad", "osci_reset")
@@ -376,8 +413,9 @@ def measure_configs(dev, stream, only=None):
     """The quantizer and GEMM workloads at Llama-3.1-8B shapes, each timed on its own.
 
     quantizer: an 8192x4096 activation (0.1% of the channels x50), deterministic H32, both axes from one
-    launch, RTNE and Philox SR (seed 1).  Cold: five copies of the tensor (335 MB, more than the 256 MB
-    last-level cache) and five output sets in rotation; hot: one.  fprop_qkv: Y = X W^T, 8192x6144x4096, H16
+    launch, RTNE and Philox SR (seed 1).  Cold: 17 copies of the tensor (1.14 GB, well past the 256 MB
+    last-level cache) and as many output sets in rotation; hot: one.  GEMMs: cold rotates copies of the
+    quantized operands past 1 GiB, hot repeats one set.  Every figure is the median of 50 or more calls.  fprop_qkv: Y = X W^T, 8192x6144x4096, H16
     on K, RTNE, bf16 out.  mlp_dgrad: dY (Laplace, spikes) times W_down as printed, 8192x4096x14336, RTNE,
     bf16 out.  mlp_wgrad: dY^T X, 14336x14336x8192, both operands column-wise with SR, fp32 out.
     """
@@ -397,8 +435,8 @@ def measure_configs(dev, stream, only=None):
         qw = api.quantize(gpu(d["w"]), axis="row", had_n=16)["row"]
         y = torch.empty((8192, 6144), dtype=torch.bfloat16, device=dev)
         api.gemm(qx, qw, out=y)
-        us = time_us(lambda i: api.gemm(qx, qw, out=y), 20, stream)
-        out["fprop_qkv"] = gemm_entry(us, 8192, 6144, 4096, "Y = X W^T, H16 on K, RTNE, bf16 out")
+        out["fprop_qkv"] = gemm_entry(time_gemm(qx, qw, y, stream), 8192, 6144, 4096,
+                                      "Y = X W^T, H16 on K, RTNE, bf16 out")
         del d, qx, qw, y
     if "mlp_dgrad" in want or "mlp_wgrad" in want:
         d = synth.mlp()
@@ -407,8 +445,8 @@ def measure_configs(dev, stream, only=None):
         qw = api.quantize(gpu(d["w"]), axis="row")["row"]
         dx = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
         api.gemm(qdr, qw, out=dx)
-        us = time_us(lambda i: api.gemm(qdr, qw, out=dx), 20, stream)
-        out["mlp_dgrad"] = gemm_entry(us, 8192, 4096, 14336, "dX = dY W_down (shapes as printed), RTNE, bf16 out")
+        out["mlp_dgrad"] = gemm_entry(time_gemm(qdr, qw, dx, stream), 8192, 4096, 14336,
+                                      "dX = dY W_down (shapes as printed), RTNE, bf16 out")
         del qdr, qw, dx
     if "osci_reset" in want and only:
         out["osci_reset"] = measure_osci(dev, stream)
@@ -417,8 +455,8 @@ def measure_configs(dev, stream, only=None):
         qx = api.quantize(gpu(d["x"]), axis="col", rounding="sr", seed=4002)["col"]
         dw = torch.empty((14336, 14336), dtype=torch.float32, device=dev)
         api.gemm(qd, qx, out=dw)
-        us = time_us(lambda i: api.gemm(qd, qx, out=dw), 10, stream)
-        out["mlp_wgrad"] = gemm_entry(us, 14336, 14336, 8192, "dW = dY^T X, column-wise SR operands, fp32 out")
+        out["mlp_wgrad"] = gemm_entry(time_gemm(qd, qx, dw, stream), 14336, 14336, 8192,
+                                      "dW = dY^T X, column-wise SR operands, fp32 out")
     return out
 
 
@@ -427,7 +465,7 @@ def measure_quantizer(x, dev, stream):
     from block_scaled_fp4_hadamard_amd import api
     rows, cols = x.shape
     nbytes = rows * cols * 2 + 2 * (rows * cols // 2 + rows * cols // 32)
-    xs = [x] + [x.clone() for _ in range(4)]
+    xs = [x] + [x.clone() for _ in range(copies_for(x.numel() * 2) - 1)]
     q = {}
     for rounding, seed in (("rtne", 0), ("sr", 1)):
         sets = [(api.empty_qtensor(rows, cols, dev), api.empty_qtensor(cols, rows, dev)) for _ in xs]
@@ -436,20 +474,21 @@ def measure_quantizer(x, dev, stream):
             api.quantize(xs[i % n], axis="both", rounding=rounding, seed=seed, had_n=32, had_kind="det",
                          row_out=sets[i % n][0], col_out=sets[i % n][1])
         run(0)
-        cold = time_us(run, 50, stream)
-        hot = time_us(lambda i: run(0), 50, stream)
+        cold = time_median_us(run, 64, stream)
+        hot = time_median_us(lambda i: run(0), 64, stream)
         gbs = nbytes / (cold * 1e-6) / 1e9
         q[rounding] = {"us_cold": round(cold, 2), "us_hot": round(hot, 2), "GB/s": round(gbs, 1),
                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     out = dict(workload="X 8192x4096 bf16, H32 deterministic, E2M1, row- and column-wise outputs from one launch",
-               bytes_per_call=nbytes, **q)
+               bytes_per_call=nbytes, timing="median of 64 calls; cold: %d input and output sets in rotation "
+               "(%.2f GB of input)" % (len(xs), len(xs) * x.numel() * 2 / 1e9), **q)
     out["rotation_ablation"] = measure_ablation(xs, sets, stream)
     return out
 
 
 def measure_ablation(xs, sets, stream):
     """The rotation's cost, fused and unfused, on the quantizer-only workload (RTNE, both outputs, the same
-    five tensors in rotation): the fused kernel without rotation, with the H32 rotation, and the rotation as
+    tensors in rotation): the fused kernel without rotation, with the H32 rotation, and the rotation as
     its own kernel (float32 y along each axis) followed by the cast of y.  The pages report ~1.06-1.07x for
     their fused kernels and ~1.4-1.6x unfused, on NVIDIA SM90/SM100 (context, not a target)."""
     import torch
@@ -469,9 +508,9 @@ def measure_ablation(xs, sets, stream):
         api.quantize_f32(yr, axis="row", out=sets[i % n][0])
         api.quantize_f32(yc, axis="col", out=sets[i % n][1])
     unfused(0)
-    t_plain = time_us(lambda i: fused(i, 0), 30, stream)
-    t_fused = time_us(lambda i: fused(i, 32), 30, stream)
-    t_unfused = time_us(unfused, 30, stream)
+    t_plain = time_median_us(lambda i: fused(i, 0), 50, stream)
+    t_fused = time_median_us(lambda i: fused(i, 32), 50, stream)
+    t_unfused = time_median_us(unfused, 50, stream)
     return {"us_unrotated": round(t_plain, 2), "us_fused_h32": round(t_fused, 2),
             "us_unfused_h32": round(t_unfused, 2), "fused_ratio": round(t_fused / t_plain, 3),
             "unfused_ratio": round(t_unfused / t_plain, 3),
@@ -493,8 +532,8 @@ def measure_osci(dev, stream, rows=14336, cols=4096):
     api.osci_reset(w, q, st, "init")
     n = rows * cols
     nbytes = int(n * (4 + 0.5 + 1 / 32 + 16 + 16))
-    track = time_us(lambda i: api.osci_reset(w, q, st, "track"), 20, stream)
-    check = time_us(lambda i: api.osci_reset(w, q, st, "check", 1e30), 20, stream)
+    track = time_median_us(lambda i: api.osci_reset(w, q, st, "track"), 50, stream)
+    check = time_median_us(lambda i: api.osci_reset(w, q, st, "check", 1e30), 50, stream)
     gbs = nbytes / (track * 1e-6) / 1e9
     return {"workload": "OsciReset on a %dx%d float32 master weight (E2M1 row-wise quantization)" % (rows, cols),
             "bytes_per_track_step": nbytes, "us_track": round(track, 2), "us_check": round(check, 2),
