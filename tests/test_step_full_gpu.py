@@ -1,0 +1,109 @@
+"""GPU parity of the benchmarked Llama-block step at its full size (8192 tokens) on sampled lines and outputs.
+
+The step is built exactly as the benchmark builds and times it: LlamaBlockStep with the default recipe at
+8192 tokens, q/k/v and gate/up as fused projections, a random-sign H32 rotation along every quantization axis,
+RTNE on activations and weights, Philox stochastic rounding on every upstream gradient ("Ripensare il Bias di
+Shrinkage ...", Metodologia 2: the UFP4 recipe), for both grids.
+
+The oracle quantizes only sampled output lines (rows of the row-wise output, columns of the column-wise one),
+each with its index in the whole tensor, so its stochastic-rounding draws are those of the full output:
+ - 20 lines per tensor and axis, always including the first and last lines and, for the stacked weights and
+   gradients, the lines on either side of each edge between stacked parts, byte for byte;
+ - every GEMM ("Pre-addestramento ... con MXFP4", Metodologia: Fprop Y = X W^T, Dgrad dX = dY W, Wgrad
+   dW = dY^T X) on the outputs whose A and B lines are among those samples, to |err| <= 1e-5 * sum |a_i b_i|
+   (bf16 outputs: plus half a bf16 ulp), the reference built from the oracle's own quantized lines.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.gemm import gemm_ref
+from oracle.quantize import quantize_ref, RTNE, SR
+from block_scaled_fp4_hadamard_amd import synth
+from block_scaled_fp4_hadamard_amd.linear_step import LlamaBlockStep, Recipe
+from gpu_helpers import announce, assert_bytes_equal, assert_gemm_close
+from test_step_gpu import PROJECTIONS, INPUT_OF, HAD, sr_seeds, part_edges
+
+pytestmark = pytest.mark.gpu
+
+TOKENS = 8192
+LINES = 20
+
+
+@pytest.fixture(scope="module")
+def host():
+    d = synth.llama_block(TOKENS)
+    ops = {v: d[v] for v in INPUT_OF.values()}
+    for proj, parts in PROJECTIONS.items():
+        ops["w_" + proj] = np.concatenate([d["w_" + p] for p in parts], axis=0)
+        ops["dy_" + proj] = np.concatenate([d["dy_" + p] for p in parts], axis=1)
+    return d, ops
+
+
+def sample_lines(n, rng, edges=()):
+    """LINES distinct indices in [0, n): the ends, both sides of each edge, the rest at random; sorted."""
+    keep = {0, n - 1}
+    for e in edges:
+        keep.update(i for i in (e - 1, e) if 0 <= i < n)
+    rest = np.setdiff1d(np.arange(n), np.fromiter(keep, dtype=np.int64))
+    pick = rng.choice(rest, max(0, LINES - len(keep)), replace=False)
+    return np.unique(np.concatenate([np.fromiter(keep, dtype=np.int64), pick]))
+
+
+def edges_of(name, axis, out_dims):
+    """Part edges along the lines of one output: stacked weights stack along rows (row-wise lines), stacked
+    gradients along columns (column-wise lines)."""
+    if name.startswith("w_") and axis == "row":
+        return part_edges(PROJECTIONS[name[2:]], out_dims)
+    if name.startswith("dy_") and axis == "col":
+        return part_edges(PROJECTIONS[name[3:]], out_dims)
+    return []
+
+
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+def test_benched_step_full_size_sampled(grid, host):
+    d, ops = host
+    announce("llama block step, %d tokens, sampled lines and outputs, %s" % (TOKENS, grid))
+    dev = torch.device("cuda:0")
+    tensors = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in d.items()}
+    step = LlamaBlockStep(tensors, Recipe(grid=grid))
+    assert len(step.launches) == 24 and sum(1 for L in step.launches if L.flops) == 12
+    step.run()
+    torch.cuda.synchronize()
+    del tensors
+
+    seeds = sr_seeds()
+    out_dims = {p: synth.LLAMA_LINEARS[p][0] for p in synth.LLAMA_LINEARS}
+    rng = np.random.default_rng(8192)
+    lines, ref = {}, {}
+    for name, a in ops.items():
+        sr = name.startswith("dy_")
+        for axis in ("row", "col"):
+            n = a.shape[0] if axis == "row" else a.shape[1]
+            ls = sample_lines(n, rng, edges_of(name, axis, out_dims))
+            r = quantize_ref(a, axis=axis, grid=grid, rounding=SR if sr else RTNE, seed=seeds[name] if sr else 0,
+                             lines=ls, **HAD)[axis]
+            q = step.q[name][axis]
+            idx = torch.from_numpy(ls).to(dev)
+            got_c = q.codes.index_select(0, idx).cpu().numpy()
+            got_s = q.scales.index_select(0, idx).cpu().numpy()
+            assert_bytes_equal(got_s, r[1], "%s %s %s scales (sampled lines)" % (grid, name, axis))
+            assert_bytes_equal(got_c, r[0], "%s %s %s codes (sampled lines)" % (grid, name, axis))
+            lines[name, axis], ref[name, axis] = ls, r
+
+    for proj in PROJECTIONS:
+        x, w, dy = INPUT_OF[proj], "w_" + proj, "dy_" + proj
+        n_out, n_in = ops[w].shape
+        gemms = (("fprop", (x, "row"), (w, "row"), n_in, "y", True),
+                 ("dgrad", (dy, "row"), (w, "col"), n_out, "dx", True),
+                 ("wgrad", (dy, "col"), (x, "col"), TOKENS, "dw", False))
+        for which, (an, aa), (bn, ba), k, key, bf16 in gemms:
+            rows, cols = lines[an, aa], lines[bn, ba]
+            a_codes, a_scales = ref[an, aa]
+            b_codes, b_scales = ref[bn, ba]
+            c_ref, gsum = gemm_ref(a_codes, a_scales, b_codes, b_scales, k, grid)
+            out = step.out[proj][key]
+            got = out.index_select(0, torch.from_numpy(rows).to(dev)).index_select(
+                1, torch.from_numpy(cols).to(dev)).float().cpu().numpy()
+            assert got.shape == (len(rows), len(cols))
+            assert_gemm_close(got, c_ref, gsum, "%s %s %s (sampled)" % (grid, which, proj), bf16=bf16)
