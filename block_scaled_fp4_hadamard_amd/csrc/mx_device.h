@@ -148,6 +148,34 @@ __device__ __forceinline__ void sr_draws(uint64_t ctr8, uint32_t stream, uint32_
   }
 }
 
+// Eight E2M1 codes of y[0..7] by stochastic rounding from one Philox block r
+// (element 2j takes the low half of word j, element 2j + 1 the high half, as
+// in sr_draws), packed element 2j in the low nibble.  gfx950's scaled
+// stochastic conversion rounds the first value of its pair with bits 31..10
+// of the random operand and the second value with bits 30..9 (checked bit for
+// bit on the GPU over random values in every E2M1 interval, both signs,
+// values on a level and the saturating band).  Each pair is converted twice,
+// with element 2j's draw placed at bits 31..16 and element 2j + 1's at bits
+// 30..15, zeros below, which is the rule of cast_one for each; the first
+// conversion's low nibble and the second's high nibble are kept.  Only the
+// selected byte of a conversion's result is defined here (the other bytes do
+// not carry the old operand through), so each is masked.  sc is the block's
+// scale as the float e8m0_scale_bits gives; y must be finite.
+__device__ __forceinline__ uint32_t sr_e2m1_8(const float* y, const U4& r, float sc) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  // the byte the conversion writes is an immediate: one statement per pair
+  const v2f p0 = {y[0], y[1]}, p1 = {y[2], y[3]}, p2 = {y[4], y[5]}, p3 = {y[6], y[7]};
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p0, r.x << 16, sc, 0) & 0x0000000Fu;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p0, (r.x >> 1) & 0x7FFF8000u, sc, 0) & 0x000000F0u;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p1, r.y << 16, sc, 1) & 0x00000F00u;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p1, (r.y >> 1) & 0x7FFF8000u, sc, 1) & 0x0000F000u;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p2, r.z << 16, sc, 2) & 0x000F0000u;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p2, (r.z >> 1) & 0x7FFF8000u, sc, 2) & 0x00F00000u;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p3, r.w << 16, sc, 3) & 0x0F000000u;
+  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p3, (r.w >> 1) & 0x7FFF8000u, sc, 3) & 0xF0000000u;
+  return c;
+}
+
 // The operand of one element at index i (see sr_draws).
 __device__ __forceinline__ uint32_t sr_draw_one(uint64_t i, uint32_t stream, uint32_t k0, uint32_t k1) {
   const uint64_t g = i >> 3;

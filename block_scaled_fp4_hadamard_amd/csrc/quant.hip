@@ -116,6 +116,16 @@ __device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ct
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 6], y[8 * d + 7], sc, 3);
       w[d] = r;
     }
+  } else if constexpr (GRID == MX_GRID_E2M1) {
+    // stochastic rounding on gfx950's conversion, a pair per instruction twice over (sr_e2m1_8)
+    const float sc = __uint_as_float(e8m0_scale_bits(byte));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      U4 ph[2];
+      philox4x32_10_xn<2>(ctr8 + 2 * hh, stream, k0, k1, ph);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) w[2 * hh + d] = sr_e2m1_8(&y[16 * hh + 8 * d], ph[d], sc);
+    }
   } else {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {                 // 16 outputs (two Philox calls) at a time
@@ -270,6 +280,13 @@ __device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int la
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 6], y[8 * d + 7], sc, 3);
       w[d] = r;
     }
+  } else if constexpr (GRID == MX_GRID_E2M1) {
+    // stochastic rounding on gfx950's conversion, a pair per instruction twice over (sr_e2m1_8)
+    const float sc = __uint_as_float(e8m0_scale_bits(byte));
+    U4 ph[2];
+    philox4x32_10_xn<2>(ctr8, stream, k0, k1, ph);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) w[d] = sr_e2m1_8(&y[8 * d], ph[d], sc);
   } else {
     uint32_t u[16] = {};
     if constexpr (ROUND == MX_ROUND_SR) sr_draws<2>(ctr8, stream, k0, k1, u);
