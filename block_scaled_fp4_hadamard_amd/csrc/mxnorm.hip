@@ -147,6 +147,11 @@ __device__ __forceinline__ uint32_t cast8(const uint4& v, uint32_t xmax, float r
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], sc, 1);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], sc, 2);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], sc, 3);
+  } else if constexpr (GRID == MX_GRID_E2M1) {
+    // stochastic rounding, a pair per conversion twice over (non-finite blocks are zeroed below)
+    U4 ph[1];
+    philox4x32_10_xn<1>((uint64_t)elem >> 3, 0u, k0, k1, ph);                 // elem % 8 == 0
+    r = sr_e2m1_8(y, ph[0], __uint_as_float(e8m0_scale_bits(byte)));
   } else {
     uint32_t u[8] = {};
     if constexpr (ROUND == MX_ROUND_SR) sr_draws<1>((uint64_t)elem >> 3, 0u, k0, k1, u);   // elem % 8 == 0

@@ -103,8 +103,12 @@ __device__ __forceinline__ int64_t tile_div(int64_t a, int64_t b) {
 template <int MODE, int GRID, int ROUND, class Get>
 __device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax128, uint64_t ctr8, uint32_t stream,
                                          uint32_t k0, uint32_t k1, uint32_t& scale, float& so_out) {
+  // stochastic rounding: the E2M1 casts take whole Philox blocks (sr_e2m1_8), the E1M2 one per-element draws
+  constexpr bool kSrE2M1 = ROUND == MX_ROUND_SR && (GRID == MX_GRID_E2M1 || MODE != 0);
   uint32_t u[16] = {};
-  if constexpr (ROUND == MX_ROUND_SR) sr_draws<2>(ctr8, stream, k0, k1, u);
+  U4 ph[2];
+  if constexpr (kSrE2M1) philox4x32_10_xn<2>(ctr8, stream, k0, k1, ph);
+  else if constexpr (ROUND == MX_ROUND_SR) sr_draws<2>(ctr8, stream, k0, k1, u);
   uint32_t w[2] = {0u, 0u};
   bool zero_codes;
   if constexpr (MODE == 0) {
@@ -122,6 +126,13 @@ __device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(get(8 * h + 6)), __uint_as_float(get(8 * h + 7)), sc, 3);
         w[h] = r;
       }
+    } else if constexpr (kSrE2M1) {
+      const float sc = __uint_as_float(e8m0_scale_bits(byte));      // non-finite blocks are zeroed below
+      float yy[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) yy[k] = __uint_as_float(get(k));
+      w[0] = sr_e2m1_8(&yy[0], ph[0], sc);
+      w[1] = sr_e2m1_8(&yy[8], ph[1], sc);
     } else {
 #pragma unroll
       for (int k = 0; k < 16; ++k) w[k >> 3] |= cast_one<GRID, ROUND>(__uint_as_float(get(k)), byte, u[k]) << (4 * (k & 7));
@@ -155,8 +166,8 @@ __device__ __forceinline__ uint2 quant16(Get get, uint32_t amax16, uint32_t amax
         w[h] = q;
       }
     } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) w[k >> 3] |= cast_one<MX_GRID_E2M1, ROUND>(y[k], 127u, u[k]) << (4 * (k & 7));
+      w[0] = sr_e2m1_8(&y[0], ph[0], 1.0f);                         // unit scale: byte 127
+      w[1] = sr_e2m1_8(&y[8], ph[1], 1.0f);
     }
   }
   if (zero_codes) w[0] = w[1] = 0u;
