@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t cast_block(const float (&y)[32], uint64_t ct
     const float sc = __uint_as_float(e8m0_scale_bits(byte));
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      uint32_t r = 0;
+      uint32_t r = __float_as_uint(y[8 * d]);        // any value: the four conversions write all four bytes
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 0], y[8 * d + 1], sc, 0);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 2], y[8 * d + 3], sc, 1);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 4], y[8 * d + 5], sc, 2);
@@ -260,20 +260,20 @@ __device__ __forceinline__ uint32_t split_low(uint32_t w, uint32_t t2) {
 // the other half is in lane l ^ 32.  Writes 2 code dwords; returns the scale
 // byte.  For SR, ctr8 is the element index of y[0] / 8.
 template <int GRID, int ROUND>
-__device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], int lane, uint64_t ctr8, uint32_t stream,
+__device__ __forceinline__ uint32_t cast_half_block(const float (&y)[16], uint64_t ctr8, uint32_t stream,
                                                     uint32_t k0, uint32_t k1, uint32_t (&w)[2]) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(y[i]));
   const uint32_t mb = __float_as_uint(m);
+  // one of the swap's two results is the lane's own value and the other its partner's (lane l ^ 32)
   const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
-  const uint32_t other = lane < 32 ? sw[1] : sw[0];
-  const uint32_t byte = scale_byte<GRID>(max(mb, other) >> 23);
+  const uint32_t byte = scale_byte<GRID>(max(sw[0], sw[1]) >> 23);
   if constexpr (GRID == MX_GRID_E2M1 && ROUND == MX_ROUND_RTNE) {
     const float sc = __uint_as_float(e8m0_scale_bits(byte));
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      uint32_t r = 0;
+      uint32_t r = __float_as_uint(y[8 * d]);        // any value: the four conversions write all four bytes
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 0], y[8 * d + 1], sc, 0);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 2], y[8 * d + 3], sc, 1);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[8 * d + 4], y[8 * d + 5], sc, 2);
@@ -709,7 +709,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       // counter of the lane's first output: (row * cols + c0) / 8 + 2 hl; group g is 4 rows further, and
       // cols % 8 == 0
       const uint32_t byte =
-          cast_half_block<GRID, ROUND>(y, lane, ctr0 + (uint64_t)g * (uint64_t)(p.cols >> 1), 0u, k0, k1, w);
+          cast_half_block<GRID, ROUND>(y, ctr0 + (uint64_t)g * (uint64_t)(p.cols >> 1), 0u, k0, k1, w);
       typedef unsigned int u2v __attribute__((ext_vector_type(2)));
       if constexpr (FAST) {
         *(__attribute__((address_space(1))) u2v*)(cbase_u + (uint64_t)(coff + (uint32_t)(4 * g) * (uint32_t)p.ld_row_codes)) =
@@ -763,7 +763,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       const int64_t cc = cl + 32 * g;
       uint32_t w[2];
       // counter: (cc * rows + row0) / 8 + 2 hl with cc 32 g columns further, and rows % 32 == 0 here
-      const uint32_t byte = cast_half_block<GRID, ROUND>(y, lane, cctr0 + (uint64_t)(4 * g) * (uint64_t)p.rows, 1u, k0,
+      const uint32_t byte = cast_half_block<GRID, ROUND>(y, cctr0 + (uint64_t)(4 * g) * (uint64_t)p.rows, 1u, k0,
                                                          k1, w);
       if constexpr (FAST) {
         typedef unsigned int u2c __attribute__((ext_vector_type(2)));
