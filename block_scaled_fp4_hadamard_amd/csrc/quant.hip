@@ -517,10 +517,17 @@ __device__ __forceinline__ void issue_tile(const QuantParams& p, int64_t row0, i
   const uint32_t off0 = (uint32_t)(((8 * wave + hr) * p.ld_x + 8 * pg) * 2);
   const uint32_t step = (uint32_t)(4 * p.ld_x);                 // two rows of bf16, in bytes
   const bool interior = row0 + kTileRows <= p.rows && col0 + kTileCols <= p.cols;
+  if (interior) {
+    // straight-line: the wave's LDS rows from one scalar base, no per-copy tests
+    const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(buf + 8 * wave * kRowBytes));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(base, off0 + (uint32_t)i * step, lbase + (uint32_t)(2 * i * kRowBytes));
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * wave + 2 * i + hr;
-    if (interior || (row0 + r < p.rows && col0 + 8 * pg < p.cols))
+    if (row0 + r < p.rows && col0 + 8 * pg < p.cols)
       dma16(base, off0 + (uint32_t)i * step, lds_addr(buf + (8 * wave + 2 * i) * kRowBytes));
     else
       *(uint4*)(buf + r * kRowBytes + ps * 16) = uint4{0u, 0u, 0u, 0u};
@@ -535,23 +542,21 @@ __device__ __forceinline__ uint32_t dpp_x2(uint32_t v) { return (uint32_t)__buil
 __device__ __forceinline__ uint32_t dpp_hm(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false); }
 __device__ __forceinline__ uint32_t dpp_m(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false); }
 
-// max / min over the whole wave (every lane active): the 16-lane rows by DPP,
-// then the four rows' first lanes
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  v = max(v, dpp_x1(v));
-  v = max(v, dpp_x2(v));
-  v = max(v, dpp_hm(v));
-  v = max(v, dpp_m(v));
-  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+// Packed 16-bit maxima over the whole wave (every lane active): each row of
+// 16 lanes by quad, half-row and row mirror exchanges; then rows 1 and 3 take
+// the last lane of rows 0 and 2 (row_bcast:15), and rows 2 and 3 take lane 31
+// (row_bcast:31), so that lane 63 holds the maxima of all 64 lanes.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
 }
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-  v = min(v, dpp_x1(v));
-  v = min(v, dpp_x2(v));
-  v = min(v, dpp_hm(v));
-  v = min(v, dpp_m(v));
-  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+__device__ __forceinline__ uint32_t wave_pk_max_u16(uint32_t v) {
+  v = pk_max_u16(v, dpp_x1(v));
+  v = pk_max_u16(v, dpp_x2(v));
+  v = pk_max_u16(v, dpp_hm(v));
+  v = pk_max_u16(v, dpp_m(v));
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Scale bytes of 8 consecutive blocks of a row, held by lanes 8a .. 8a+7
@@ -784,7 +789,7 @@ template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(wgs_per_cu(ROUND))))
 quant_kernel(const QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kPartBytes];   // two tile buffers
-  __shared__ uint32_t red[2 * (kThreads / 64)];
+  __shared__ uint32_t red[kThreads / 64];
   __shared__ uint4 htab[2 * 64];       // the sign-Hadamard MFMA operand of each lane (two K-halves)
   __shared__ uint16_t fix[2 * kThreads];   // blocks of a kClsSpecial tile to redo exactly
   __shared__ uint32_t fix_n;
@@ -840,16 +845,14 @@ quant_kernel(const QuantParams p) {
         mn2 = __builtin_elementwise_min(mn2, m - (us2){1, 1});  // zero wraps to 0xFFFF: ignored
       }
     }
-    uint32_t mx = wave_max(max((uint32_t)mx2.x, (uint32_t)mx2.y));
-    uint32_t mn = wave_min(min((uint32_t)mn2.x, (uint32_t)mn2.y));
-    if (lane == 0) {
-      red[wave] = mx;
-      red[4 + wave] = mn;
-    }
+    // both reductions in one: max |x| in the high half, 0xFFFF - (min nonzero |x| - 1) in the low
+    const uint32_t lmx = max((uint32_t)mx2.x, (uint32_t)mx2.y), lmn = min((uint32_t)mn2.x, (uint32_t)mn2.y);
+    const uint32_t both = wave_pk_max_u16((lmx << 16) | (0xFFFFu - lmn));
+    if (lane == 0) red[wave] = both;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
-    mx = max(max(red[0], red[1]), max(red[2], red[3]));
-    mn = min(min(red[4], red[5]), min(red[6], red[7]));
+    const uint32_t all = pk_max_u16(pk_max_u16(red[0], red[1]), pk_max_u16(red[2], red[3]));
+    const uint32_t mx = all >> 16, mn = 0xFFFFu - (all & 0xFFFFu);
 
     // ---- 3. classify by the exponent fields of the largest and smallest nonzero |x|
     int cls = kClsMfma1;
