@@ -157,23 +157,44 @@ __device__ __forceinline__ void sr_draws(uint64_t ctr8, uint32_t stream, uint32_
 // values on a level and the saturating band).  Each pair is converted twice,
 // with element 2j's draw placed at bits 31..16 and element 2j + 1's at bits
 // 30..15, zeros below, which is the rule of cast_one for each; the first
-// conversion's low nibble and the second's high nibble are kept.  Only the
-// selected byte of a conversion's result is defined here (the other bytes do
-// not carry the old operand through), so each is masked.  sc is the block's
-// scale as the float e8m0_scale_bits gives; y must be finite.
+// conversion's low nibble and the second's high nibble are kept.
+//
+// The conversion writes only the byte its op_sel picks and keeps the other
+// three bytes of its destination (checked on the GPU against the builtin for
+// every byte position).  The compiler's builtin does not model that: it treats
+// the whole destination as written, so a chain of builtins loses all but the
+// last byte.  The conversions are therefore written as one asm block with
+// tied destinations: the four even-element conversions fill the bytes of `a`,
+// the four odd-element ones those of `b`, and one bit-field insert takes the
+// low nibbles of `a` and the high nibbles of `b`.  A VALU result written
+// through op_sel needs one wait state before another VALU instruction reads
+// it: the two chains alternate, so consecutive conversions of one chain are
+// one instruction apart, and an s_nop closes the block (another opens it, for
+// any partial write just before).  sc is the block's scale as the float
+// e8m0_scale_bits gives; y must be finite.
 __device__ __forceinline__ uint32_t sr_e2m1_8(const float* y, const U4& r, float sc) {
   typedef float v2f __attribute__((ext_vector_type(2)));
-  // the byte the conversion writes is an immediate: one statement per pair
   const v2f p0 = {y[0], y[1]}, p1 = {y[2], y[3]}, p2 = {y[4], y[5]}, p3 = {y[6], y[7]};
-  uint32_t c = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p0, r.x << 16, sc, 0) & 0x0000000Fu;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p0, (r.x >> 1) & 0x7FFF8000u, sc, 0) & 0x000000F0u;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p1, r.y << 16, sc, 1) & 0x00000F00u;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p1, (r.y >> 1) & 0x7FFF8000u, sc, 1) & 0x0000F000u;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p2, r.z << 16, sc, 2) & 0x000F0000u;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p2, (r.z >> 1) & 0x7FFF8000u, sc, 2) & 0x00F00000u;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p3, r.w << 16, sc, 3) & 0x0F000000u;
-  c |= __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p3, (r.w >> 1) & 0x7FFF8000u, sc, 3) & 0xF0000000u;
-  return c;
+  // element 2j's draw at bits 31..16, element 2j + 1's at bits 30..15
+  const uint32_t e0 = r.x << 16, e1 = r.y << 16, e2 = r.z << 16, e3 = r.w << 16;
+  const uint32_t o0 = (r.x >> 1) & 0x7FFF8000u, o1 = (r.y >> 1) & 0x7FFF8000u;
+  const uint32_t o2 = (r.z >> 1) & 0x7FFF8000u, o3 = (r.w >> 1) & 0x7FFF8000u;
+  uint32_t a, b;
+  asm("" : "=v"(a), "=v"(b));     // any start value: the four conversions of each write all four bytes
+  asm("s_nop 0\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %2, %6, %14\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %2, %7, %14\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %3, %8, %14 op_sel:[0,0,1,0]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %3, %9, %14 op_sel:[0,0,1,0]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %4, %10, %14 op_sel:[0,0,0,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %4, %11, %14 op_sel:[0,0,0,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %5, %12, %14 op_sel:[0,0,1,1]\n\t"
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %5, %13, %14 op_sel:[0,0,1,1]\n\t"
+      "s_nop 0"
+      : "+v"(a), "+v"(b)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(e0), "v"(o0), "v"(e1), "v"(o1), "v"(e2), "v"(o2), "v"(e3),
+        "v"(o3), "v"(sc));
+  return (a & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
 }
 
 // The operand of one element at index i (see sr_draws).
