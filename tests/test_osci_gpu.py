@@ -70,3 +70,55 @@ def test_trajectory_matches_the_oracle(grid, rows, cols):
             assert_bytes_equal(got, ref_state[name].view(np.uint32), "step %d %s" % (t, name))
         assert int(counter.item()) == total
     assert total > 0 and total < rows * cols          # some elements were reset, not all
+
+
+def test_full_size_sampled_rows():
+    """The benchmarked size, 14336 x 4096 float32 (E2M1, row-wise): the whole weight runs on the GPU through
+    the same ten-step trajectory, and the oracle follows 24 sampled rows, the first and last included.  Rows
+    are independent (row-wise blocks, an elementwise state update), so the sampled rows' codes, weights and
+    state must match bit for bit.  The reset count covers the whole weight and is checked against the
+    sampled rows' share only as a lower bound."""
+    rows, cols, steps = 14336, 4096, 9
+    rng = np.random.default_rng(14336)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.choice(np.arange(1, rows - 1), 22, replace=False)]))
+    modes = ["init"] + ["track"] * 3 + ["check"] + ["track"] * 3 + ["check", "check"]
+    thresholds = {4: 3.0, 8: 50.0, 9: 0.0}
+    dev = torch.device("cuda:0")
+    w0 = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    flip = np.zeros((rows, cols), dtype=bool)
+    flip[:, ::7] = True
+    w_gpu = torch.from_numpy(w0).to(dev)
+    state = api.OsciState.empty_like(w_gpu)
+    counter = torch.zeros(1, dtype=torch.int64, device=dev)
+    idx = torch.from_numpy(sample).to(dev)
+    ref_state = {}
+    w_ref = w0[sample].copy()
+    prev = w0
+    total = 0
+    for t, mode in enumerate(modes):
+        announce("osci full size e2m1 %dx%d step %d %s" % (rows, cols, t, mode))
+        if t > 0:
+            # the trajectory of the small cases, generated step by step: drift, and flips around w0
+            d = (rng.standard_normal((rows, cols)) * 1e-4).astype(np.float32)
+            sign = 1.0 if (t - 1) % 2 == 0 else -1.0
+            nxt = np.where(flip, (w0 * np.float32(1.0 + sign * 0.1)).astype(np.float32), (prev + d).astype(np.float32))
+            inc = (nxt - prev).astype(np.float32)
+            prev = nxt
+            w_gpu.add_(torch.from_numpy(inc).to(dev))        # float32 adds, as the oracle's below
+            w_ref = (w_ref + inc[sample]).astype(np.float32)
+        q = api.quantize_f32(w_gpu, axis="row", grid="e2m1")
+        thr = thresholds.get(t, 0.0)
+        api.osci_reset(w_gpu, q, state, mode, thr, resets=counter)
+        torch.cuda.synchronize()
+        codes, scales = quantize_values(w_ref, "e2m1")
+        got_codes = q.codes.index_select(0, idx).cpu().numpy()
+        assert_bytes_equal(got_codes, codes, "step %d codes (sampled rows)" % t)
+        w_ref, n = osci_reset_step(w_ref, decoded_weights(codes, scales, "e2m1", cols), ref_state, MODES[mode], thr)
+        total += n
+        got_w = w_gpu.index_select(0, idx).cpu().numpy().view(np.uint32)
+        assert_bytes_equal(got_w, w_ref.view(np.uint32), "step %d w (sampled rows)" % t)
+        for name in ("w_prev", "q_prev", "dist_m", "dist_q"):
+            got = getattr(state, name).index_select(0, idx).cpu().numpy().view(np.uint32)
+            assert_bytes_equal(got, ref_state[name].view(np.uint32), "step %d %s (sampled rows)" % (t, name))
+        assert int(counter.item()) >= total
+    assert total > 0
