@@ -72,8 +72,9 @@ constexpr float kInvSqrt16 = 0.25f;
 
 // Resident workgroups per CU in the persistent grid (one wave of each per
 // SIMD): four, or three for stochastic rounding, whose Philox draws need the
-// larger register budget.
-constexpr int wgs_per_cu(int round) { return round == MX_ROUND_SR ? 3 : 4; }
+// larger register budget, and for rotated casts of both axes, which hold a
+// third 16 KB LDS tile (the low parts the row pass hands to the column pass).
+constexpr int wgs_per_cu(int round, bool share) { return round == MX_ROUND_SR || share ? 3 : 4; }
 
 // tile classes (uniform per tile)
 constexpr int kClsMfma1 = 0;     // matrix-core sums, one part (or no rotation)
@@ -664,7 +665,11 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
 }
 
 // Row and column passes of a tile on the matrix cores, with the inputs split
-// into PARTS magnitude parts (thresholds t2, t3).
+// into PARTS magnitude parts (thresholds t2, t3).  Two-part tiles cast on both
+// axes split each element once: the row pass reads every 16-byte piece of the
+// tile exactly once, and it writes the piece's low parts to lowbuf at the same
+// offset; after a barrier the column pass reads them with the same transposed
+// reads as the inputs, and the high part is x ^ low.
 //   row pass: wave w, group g = the 32 blocks of rows 8w + 4g .. +3;
 //   column pass: wave w, group g = columns 64w + 32g .. +31.  A lane's
 //   operand (8 consecutive rows of its column) comes from two transposed LDS
@@ -675,8 +680,10 @@ __device__ __forceinline__ void lane_block_passes(const QuantParams& p, const ui
 // (QuantParams::fast_ok).  Its stores then take a wave-uniform tile base plus a
 // per-lane 32-bit offset and need no bounds tests.
 template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL, int PARTS, bool FAST>
-__device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t* buf, int t, int64_t row0, int64_t col0,
-                                            const uint4* htab, uint32_t t2, uint32_t t3, bool wide_scales) {
+__device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t* buf, uint8_t* lowbuf, int t,
+                                            int64_t row0, int64_t col0, const uint4* htab, uint32_t t2, uint32_t t3,
+                                            bool wide_scales) {
+  constexpr bool kShare = PARTS == 2 && DO_ROW && DO_COL;
   const int lane = t & 63, wave = t >> 6, hl = lane >> 5, n = lane & 31;
   const bf16x8 ha[2] = {__builtin_bit_cast(bf16x8, htab[2 * lane]), __builtin_bit_cast(bf16x8, htab[2 * lane + 1])};
   const uint32_t k0 = (uint32_t)p.seed, k1 = (uint32_t)(p.seed >> 32);
@@ -701,10 +708,12 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       uint4 part[3][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint4 v = *(const uint4*)(buf + r * kRowBytes +
-                                        lds_col(32 * k + 16 * h + 8 * hl, ((n >> 3) & 1) | ((wave & 1) << 3)));
+        const uint32_t off = (uint32_t)(r * kRowBytes) +
+                             lds_col(32 * k + 16 * h + 8 * hl, ((n >> 3) & 1) | ((wave & 1) << 3));
+        const uint4 v = *(const uint4*)(buf + off);
         uint4 ph[3];
         split_parts<PARTS>(v, t2, t3, ph);
+        if constexpr (kShare) *(uint4*)(lowbuf + off) = ph[1];
 #pragma unroll
         for (int q = 0; q < PARTS; ++q) part[q][h] = ph[q];
       }
@@ -729,6 +738,11 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       }
     }
   }
+  if constexpr (kShare) {
+    // every wave's low parts are in LDS before any column pass reads them (the
+    // clobber keeps the compiler's LDS accesses on their side of the barrier)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   if constexpr (DO_COL) {
     const int g16 = lane >> 4, s = lane & 15;
     // the lane's output column in group 0 and its addresses; group g is 32 columns further
@@ -747,21 +761,33 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
       uint4 part[3][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        uint32_t d[4];
+        uint32_t d[4], lo[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int row = 16 * h + 8 * (g16 >> 1) + 4 * half + (s >> 2);
+          const uint32_t off = (uint32_t)(row * kRowBytes) + lds_col(col, row & 9);
           typedef short v4s __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) v4s* lds_v4s;
           const v4s q = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)((__attribute__((address_space(3))) uint8_t*)(uint8_t*)buf +
-                                                       row * kRowBytes + lds_col(col, row & 9)));
+              (lds_v4s)((__attribute__((address_space(3))) uint8_t*)(uint8_t*)buf + off));
           d[2 * half] = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
           d[2 * half + 1] = (uint32_t)(uint16_t)q[2] | ((uint32_t)(uint16_t)q[3] << 16);
+          if constexpr (kShare) {
+            const v4s ql = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s)((__attribute__((address_space(3))) uint8_t*)lowbuf + off));
+            lo[2 * half] = (uint32_t)(uint16_t)ql[0] | ((uint32_t)(uint16_t)ql[1] << 16);
+            lo[2 * half + 1] = (uint32_t)(uint16_t)ql[2] | ((uint32_t)(uint16_t)ql[3] << 16);
+          }
         }
-        uint4 ph[3];
-        split_parts<PARTS>(uint4{d[0], d[1], d[2], d[3]}, t2, t3, ph);
+        if constexpr (kShare) {
+          part[0][h] = uint4{d[0] ^ lo[0], d[1] ^ lo[1], d[2] ^ lo[2], d[3] ^ lo[3]};
+          part[1][h] = uint4{lo[0], lo[1], lo[2], lo[3]};
+        } else {
+          uint4 ph[3];
+          split_parts<PARTS>(uint4{d[0], d[1], d[2], d[3]}, t2, t3, ph);
 #pragma unroll
-        for (int q = 0; q < PARTS; ++q) part[q][h] = ph[q];
+          for (int q = 0; q < PARTS; ++q) part[q][h] = ph[q];
+        }
       }
       float y[16];
       mfma_block_sums<PARTS>(ha, part, c, y);
@@ -786,9 +812,11 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
 }
 
 template <int HAD, int GRID, int ROUND, bool DO_ROW, bool DO_COL>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(wgs_per_cu(ROUND))))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(wgs_per_cu(ROUND, HAD > 0 && DO_ROW && DO_COL))))
 quant_kernel(const QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kPartBytes];   // two tile buffers
+  // the low parts of a two-part tile, handed from the row pass to the column pass
+  __shared__ __attribute__((aligned(16))) uint8_t lowbuf[HAD > 0 && DO_ROW && DO_COL ? kPartBytes : 16];
   __shared__ uint32_t red[kThreads / 64];
   __shared__ uint4 htab[2 * 64];       // the sign-Hadamard MFMA operand of each lane (two K-halves)
   __shared__ uint16_t fix[2 * kThreads];   // blocks of a kClsSpecial tile to redo exactly
@@ -879,13 +907,13 @@ quant_kernel(const QuantParams p) {
         const bool fast = p.fast_ok && (!DO_ROW || wide_scales) && row0 + kTileRows <= p.rows &&
                           col0 + kTileCols <= p.cols;
         if (fast) {
-          if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1, true>(p, buf, t, row0, col0, htab, t2, t3, true);
-          else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2, true>(p, buf, t, row0, col0, htab, t2, t3, true);
-          else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3, true>(p, buf, t, row0, col0, htab, t2, t3, true);
+          if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1, true>(p, buf, lowbuf, t, row0, col0, htab, t2, t3, true);
+          else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2, true>(p, buf, lowbuf, t, row0, col0, htab, t2, t3, true);
+          else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3, true>(p, buf, lowbuf, t, row0, col0, htab, t2, t3, true);
         } else {
-          if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1, false>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
-          else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2, false>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
-          else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3, false>(p, buf, t, row0, col0, htab, t2, t3, wide_scales);
+          if (cls == kClsMfma1) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 1, false>(p, buf, lowbuf, t, row0, col0, htab, t2, t3, wide_scales);
+          else if (cls == kClsMfma2) mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 2, false>(p, buf, lowbuf, t, row0, col0, htab, t2, t3, wide_scales);
+          else mfma_passes<HAD, GRID, ROUND, DO_ROW, DO_COL, 3, false>(p, buf, lowbuf, t, row0, col0, htab, t2, t3, wide_scales);
         }
       }
     } else {
@@ -939,7 +967,7 @@ hipError_t launch_quant(QuantParams p, int had_n, bool rht, int grid_kind, int r
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  const int64_t wgs_per_xcd = std::max<int64_t>(1, (int64_t)cus * wgs_per_cu(round) / 8);
+  const int64_t wgs_per_xcd = std::max<int64_t>(1, (int64_t)cus * wgs_per_cu(round, had_n > 0 && do_row && do_col) / 8);
   const dim3 g((unsigned)(8 * std::min(per_xcd, wgs_per_xcd)));
   if (!rht) p.sign_mask = 0u;
   if (had_n == 0) return launch_cast<0>(p, grid_kind, round, do_row, do_col, g, s);
