@@ -703,7 +703,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const uint64_t ctr0 = (((uint64_t)rl * (uint64_t)p.cols + (uint64_t)(col0 + 32 * (n & 7))) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      __builtin_amdgcn_sched_barrier(0);
+      
       const int r = 8 * wave + 4 * g + (n >> 3), k = n & 7;
       uint4 part[3][2];
 #pragma unroll
@@ -756,7 +756,7 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const uint64_t cctr0 = (((uint64_t)cl * (uint64_t)p.rows + (uint64_t)row0) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      __builtin_amdgcn_sched_barrier(0);
+      
       const int col = 64 * wave + 32 * g + 16 * (g16 & 1) + 4 * (s & 3);    // this lane's source columns
       uint4 part[3][2];
 #pragma unroll
