@@ -10,7 +10,9 @@
 //      of bank conflicts), and the next tile's loads are issued;
 //   3. row pass (blocks of 32 along a row: the Fprop/Dgrad operand) and
 //      column pass (blocks of 32 down a column: the Wgrad operand, written
-//      transposed).
+//      transposed).  When both run on a tile split into two magnitude parts
+//      (below), the row pass hands its low parts to the column pass through a
+//      third LDS tile, so each element is split once.
 //
 // The rotation of a 32-element block (deterministic H16/H32 or random-sign
 // RHT, "Pre-addestramento ... con MXFP4", Metodologia) is defined as
@@ -703,7 +705,6 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const uint64_t ctr0 = (((uint64_t)rl * (uint64_t)p.cols + (uint64_t)(col0 + 32 * (n & 7))) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      
       const int r = 8 * wave + 4 * g + (n >> 3), k = n & 7;
       uint4 part[3][2];
 #pragma unroll
@@ -756,7 +757,6 @@ __device__ __forceinline__ void mfma_passes(const QuantParams& p, const uint8_t*
     const uint64_t cctr0 = (((uint64_t)cl * (uint64_t)p.rows + (uint64_t)row0) >> 3) + 2 * hl;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      
       const int col = 64 * wave + 32 * g + 16 * (g16 & 1) + 4 * (s & 3);    // this lane's source columns
       uint4 part[3][2];
 #pragma unroll
