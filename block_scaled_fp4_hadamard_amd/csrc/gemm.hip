@@ -16,9 +16,12 @@
 // (every value k/4 is exact in E4M3), converted after the LDS read; the
 // FP6 E2M3 form (s << 5) | (k << 1) is kept as the alternative carrier.
 //
-// Tiling: a 256-lane workgroup owns a 256x256 block of C (four waves of
-// 128x128 = 4x4 MFMA tiles), K advances 128 elements (64 bytes per row) per
-// step through LDS; the next step's global loads are issued before the MFMAs.
+// Tiling: every kernel gives a workgroup 256x256 blocks of C.  The whole-tile
+// kernel (the hot path) is persistent, one 512-lane workgroup per CU: eight
+// waves of 128x64 (4x2 MFMA tiles), K advancing 256 elements (128 bytes per
+// row) per step, the next step copied global -> LDS by DMA while the MFMAs
+// consume the current one.  The general kernel (any shape) uses four waves of
+// 128x128, K advancing 128 elements per step through bounds-checked loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "mx_kernels.h"
