@@ -36,16 +36,18 @@ __device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u
     // other result bytes are not kept)
     return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (v2f){yy, 0.0f}, u, sc, 0) & 0xFu;
   } else {
-    // uniform grid: magnitude code = |y| * 2^(2-e), rounded
+    // uniform grid: magnitude code = t = |y| * 2^(2-e), rounded (t < 8 in a finite block)
     const int ebias = (int)byte - 127;
-    const float t = ldexpf(fabsf(yy), 2 - ebias);
     uint32_t k;
     if constexpr (ROUND == MX_ROUND_RTNE) {
-      k = (uint32_t)rintf(t);
+      k = (uint32_t)rintf(ldexpf(fabsf(yy), 2 - ebias));
     } else {
-      const float fl = floorf(t);
-      const uint32_t p22 = (uint32_t)ldexpf(t - fl, 22);     // floor(frac * 2^22); t - fl is exact
-      k = (uint32_t)fl + ((p22 + (u >> 10)) >> 22);
+      // u holds the 16-bit draw r in its top half.  T = floor(t * 2^16) (exact scaling, truncating
+      // conversion) is floor(t) * 2^16 + floor(f * 2^16), so floor(t) rounds up iff floor(f * 2^16) + r >= 2^16,
+      // that is k = (T + r) >> 16: the high word of T * 2^16 + u, one 32x32 -> 64 multiply-add.  NaN converts
+      // to T = 0 and Inf to T = 2^32 - 1, as the codes of such blocks are never kept.
+      const uint32_t T = (uint32_t)ldexpf(fabsf(yy), 18 - ebias);
+      k = (uint32_t)(((uint64_t)T * 65536u + u) >> 32);
     }
     return min(k, 7u) | ((__float_as_uint(yy) >> 28) & 8u);
   }
