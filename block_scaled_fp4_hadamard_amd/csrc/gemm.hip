@@ -456,10 +456,8 @@ __device__ __forceinline__ void load_quarter(Frags<NT>& f, const uint8_t* a, con
 
 // the 8 MFMAs of one quarter; OPSEL picks the scale byte pair (quarters 0,2 -> 0; 1,3 -> 2)
 // Lanes 32-63 hold the odd 32-block of each 64-deep quarter: their scale is
-// one byte above the even block's, so their dwords are shifted by 8.  FIRST:
-// the tile's first quarter, which starts the sums from an inline zero instead
-// of the accumulators (no zeroing moves between tiles).
-template <int GRID, int OPSEL, int NT, bool FIRST = false>
+// one byte above the even block's, so their dwords are shifted by 8.
+template <int GRID, int OPSEL, int NT>
 __device__ __forceinline__ void mfma_quarter(const Frags<NT>& f, v16f (&acc)[4][NT], int shift) {
   constexpr int kFmt = mfma_fmt<GRID>();
   v8i bj[NT];
@@ -475,8 +473,8 @@ __device__ __forceinline__ void mfma_quarter(const Frags<NT>& f, v16f (&acc)[4][
     const int sai = (int)(f.sa[i] >> shift);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, bj[j], FIRST ? v16f{} : acc[i][j], kFmt, kFmt,
-                                                                  OPSEL, sai, OPSEL, sbj[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ai, bj[j], acc[i][j], kFmt, kFmt, OPSEL, sai, OPSEL,
+                                                                  sbj[j]);
   }
   // the MFMAs are side-effect free; an empty volatile asm on their results keeps
   // them at this point of the pipeline instead of being sunk past later phases
@@ -662,8 +660,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       const int vb = blocks_in(kt);
       load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt == 0) mfma_quarter<GRID, 0, NT, true>(f0, acc, shift);
-      else mfma_quarter<GRID, 0, NT>(f0, acc, shift);
+      mfma_quarter<GRID, 0, NT>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
       load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane, vb, f1);
       __builtin_amdgcn_sched_barrier(0);
@@ -691,6 +688,12 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
     }
     store_tile_wide<OUT, 4, NT, W16>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc);
     if (rn >= w.rounds) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
     r = rn;
     bm = nbm;
     bn = nbn;
