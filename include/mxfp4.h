@@ -152,7 +152,7 @@ mx_status mx_hadamard_quantize(const uint16_t *x, int64_t rows, int64_t cols, in
  *   b          N lines of length K (codes [N][K/2], scales [N][K/32])
  *   M, N, K    >= 0 (any 0: nothing to do; K == 0 is rejected); K % 32 == 0
  *   grid       the grid both operands were quantized to (E1M2 runs as exact
- *              FP6 E2M3 on the matrix units)
+ *              FP8 E4M3 on the matrix units: every value k/4 is exact there)
  *   block      32
  *   c          device, row-major [M][ldc] fp32 or bf16 (round to nearest even
  *              of the fp32 result); aligned to its element size, ldc >= N
