@@ -153,9 +153,6 @@ __device__ __forceinline__ bool map_tile(const TileMap& tm, int& bm, int& bn) {
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitLgkm0 = 0xC07F;
 
 // Fragments of one K step from an LDS stage and its MFMAs: the wave owns
 // MT x NT 32x32 tiles at rows r0 + 32i, columns c0 + 32j of the block.
@@ -643,8 +640,9 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   Frags<NT> f0, f1;
   const int shift = 8 * (lane >> 5);
   issue(bm, bn, 0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __builtin_amdgcn_s_barrier();
+  // the waits and the barrier in one asm statement: its memory clobber keeps the compiler's LDS
+  // accesses on their side of the barrier (the barrier builtin alone is not a memory operation)
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   if (nk > 1) issue(bm, bn, 1, 1);
   else if (rn < w.rounds) issue(nbm, nbn, 0, 1);
   load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0), f1);
@@ -674,9 +672,7 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       if (more) {
         // the next step's stage has landed for this wave; every wave has read
         // its last fragments of this stage; then refill it two steps ahead
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + 2 < nk) issue(bm, bn, kt + 2, st);
         else if (rn < w.rounds && kt + 2 - nk < nk) issue(nbm, nbn, kt + 2 - nk, st);
         st ^= 1;

@@ -877,8 +877,9 @@ quant_kernel(const QuantParams p) {
     const uint32_t lmx = max((uint32_t)mx2.x, (uint32_t)mx2.y), lmn = min((uint32_t)mn2.x, (uint32_t)mn2.y);
     const uint32_t both = wave_pk_max_u16((lmx << 16) | (0xFFFFu - lmn));
     if (lane == 0) red[wave] = both;
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
+    // the wait and the barrier in one asm statement whose memory clobber keeps red[] accesses on their
+    // side of it (the barrier builtin alone is not a memory operation)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const uint32_t all = pk_max_u16(pk_max_u16(red[0], red[1]), pk_max_u16(red[2], red[3]));
     const uint32_t mx = all >> 16, mn = 0xFFFFu - (all & 0xFFFFu);
 
