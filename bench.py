@@ -9,10 +9,14 @@ weights, Philox stochastic rounding for gradients), then the Fprop, Dgrad and
 Wgrad MXFP4 GEMMs run with fp32 accumulation (bf16 Y and dX, fp32 dW).
 By default q/k/v and gate/up run as fused projections (qkv, gate_up: the
 same products and flops in 12 GEMMs and 12 quantizations); --unfused runs
-one GEMM per linear (21 GEMMs, 18 quantizations).  Inputs are seeded
-synthetic tensors of the real shapes, resident in HBM before timing starts.
+one GEMM per linear (21 GEMMs, 18 quantizations).  The Wgrads whose tiles
+leave the GEMM's last 256-tile round part-empty (qkv and down when fused) run
+as one grouped launch at the end of the step, since nothing reads dW before the
+optimizer step; --separate-wgrad runs each Wgrad after its projection's Dgrad.
+Inputs are seeded synthetic tensors of the real shapes, resident in HBM before
+timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--unfused]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--unfused] [--separate-wgrad]
     python bench.py --calibrate-copy BYTES     (device copies of BYTES, for traffic-counter scaling)
     python bench.py --workloads-only           (only the per-workload timings, for profiler runs)
     python bench.py --step-only                (only the step's timing, kernels and roofline)
@@ -55,6 +59,9 @@ def parse():
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     ap.add_argument("--unfused", action="store_true", help="one GEMM per linear instead of fused qkv and gate_up")
+    ap.add_argument("--separate-wgrad", action="store_true",
+                    help="every Wgrad in its own launch, right after its projection's Dgrad, instead of grouping "
+                         "those whose tiles leave the last GEMM round part-empty")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only the probes: the FP4 MFMA rate on register-resident zero, constant and random operands, "
                          "and the issue cost of the cast's vector instructions")
@@ -571,7 +578,7 @@ def main():
     del host
     torch.cuda.synchronize()
     log("inputs ready in %.1f s" % (time.time() - t0))
-    step = LlamaBlockStep(tensors, Recipe(grid=args.grid, fuse=not args.unfused))
+    step = LlamaBlockStep(tensors, Recipe(grid=args.grid, fuse=not args.unfused, group_wgrad=not args.separate_wgrad))
 
     for _ in range(args.warmup):
         step.run()
@@ -605,7 +612,7 @@ def main():
     block16 = measure_block16(tensors, dev)
     # the same step on the other grid (the uniform E1M2 grid's GEMMs run on the FP8 matrix path)
     other = "e1m2" if args.grid == "e2m1" else "e2m1"
-    step2 = LlamaBlockStep(tensors, Recipe(grid=other, fuse=not args.unfused))
+    step2 = LlamaBlockStep(tensors, Recipe(grid=other, fuse=not args.unfused, group_wgrad=not args.separate_wgrad))
     step2.run()
     ms2, fam2 = time_step(step2, max(3, args.steps // 2), stream)
     other_step = {"grid": other, "ms_per_step": round(ms2, 4),
@@ -642,7 +649,8 @@ def main():
                                (args.tokens, args.grid, ", one GEMM per linear" if args.unfused else
                                 ", q/k/v and gate/up as fused projections"),
                    "tokens": args.tokens, "d_model": 4096, "d_kv": 1024, "d_ffn": 14336,
-                   "gemms": sum(1 for L in step.launches if L.flops),
+                   "gemms": step.gemms, "gemm_launches": sum(1 for L in step.launches if L.flops),
+                   "grouped_wgrad": [L.name for L in step.launches if L.gemms > 1],
                    "quantize_launches": sum(1 for L in step.launches if not L.flops), "fused_projections":
                    not args.unfused, "grid": args.grid, "gemm_tflop_per_step": round(step.flops / 1e12, 3),
                    "quant_gb_per_step": round(step.quant_bytes / 1e9, 3)},

@@ -17,7 +17,7 @@ HAD = {"none": 0, "det": 1, "rand": 2}
 OUT = {"f32": 0, "bf16": 1}
 OSCI = {"init": 0, "track": 1, "check": 2}
 
-EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_mxnorm_quantize", "mx_quant_stats",
+EXPORTS = ("mx_quantize", "mx_hadamard_quantize", "mx_gemm", "mx_gemm_grouped", "mx_mxnorm_quantize", "mx_quant_stats",
            "mx_nvfp4_quantize", "mx_hadamard_rotate", "mx_quantize_f32", "mx_osci_reset", "mx_status_str",
            "mx_version")
 
@@ -39,6 +39,14 @@ class QTensorC(ctypes.Structure):
                 ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64)]
 
 
+GEMM_GROUP_MAX = 8      # MX_GEMM_GROUP_MAX
+
+
+class GemmProblemC(ctypes.Structure):
+    _fields_ = [("a", ctypes.POINTER(QTensorC)), ("b", ctypes.POINTER(QTensorC)),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("c", ctypes.c_void_p), ("ldc", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -57,6 +65,8 @@ def lib():
         L.mx_hadamard_quantize.restype = ctypes.c_int
         L.mx_gemm.argtypes = [qp, qp, i64, i64, i64, i32, i32, vp, i64, i32, vp]
         L.mx_gemm.restype = ctypes.c_int
+        L.mx_gemm_grouped.argtypes = [ctypes.POINTER(GemmProblemC), i32, i64, i32, i32, i32, vp]
+        L.mx_gemm_grouped.restype = ctypes.c_int
         L.mx_mxnorm_quantize.argtypes = [vp, i64, i64, i64, i32, ctypes.c_float, i32, i32, u64, qp, vp, vp]
         L.mx_mxnorm_quantize.restype = ctypes.c_int
         L.mx_quant_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, qp, vp, vp]
@@ -106,6 +116,15 @@ def mx_hadamard_quantize(x_ptr, rows, cols, ld_x, block, grid, rnd, axis, seed, 
 
 def mx_gemm(a_q, b_q, M, N, K, grid, block, c_ptr, ldc, out, stream):
     return lib().mx_gemm(ctypes.byref(a_q), ctypes.byref(b_q), M, N, K, grid, block, c_ptr, ldc, out, stream)
+
+
+def mx_gemm_grouped(problems, K, grid, block, out, stream):
+    """problems: list of (a QTensorC, b QTensorC, M, N, c_ptr, ldc)."""
+    qs = [(a, b) for a, b, *_ in problems]     # kept alive through the call
+    arr = (GemmProblemC * max(1, len(problems)))()
+    for i, ((a, b), (_, _, M, N, c_ptr, ldc)) in enumerate(zip(qs, problems)):
+        arr[i] = GemmProblemC(ctypes.pointer(a), ctypes.pointer(b), M, N, c_ptr, ldc)
+    return lib().mx_gemm_grouped(arr, len(problems), K, grid, block, out, stream)
 
 
 def mx_mxnorm_quantize(x_ptr, rows, cols, ld_x, power, c, grid, rnd, seed, out_q, rho_ptr, stream):

@@ -8,6 +8,8 @@ import torch
 
 from . import _lib
 
+GEMM_GROUP_MAX = _lib.GEMM_GROUP_MAX    # problems per gemm_grouped call
+
 
 @dataclass
 class QTensor:
@@ -114,11 +116,48 @@ def gemm(a, b, out_dtype=torch.float32, out=None, grid=None):
     M, N, K = a.lines, b.lines, a.k
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    elif out.dim() != 2 or out.shape[0] != M or out.shape[1] != N or out.stride(1) != 1:
+        raise ValueError("out must be a row-major (%d, %d) view" % (M, N))
     kind = {torch.float32: "f32", torch.bfloat16: "bf16"}[out.dtype]
     st = _lib.mx_gemm(a.c_struct(), b.c_struct(), M, N, K, _lib.GRID[grid], a.block, out.data_ptr(), out.stride(0),
                       _lib.OUT[kind], _stream(out.device))
     _lib.check(st, "mx_gemm")
     return out
+
+
+def gemm_grouped(problems, grid=None):
+    """Several GEMMs C_i = A_i B_i^T of one K, grid and output dtype in one library call.
+
+    problems: list of (a, b, out) with out a preallocated (M_i, N_i) fp32 or bf16 tensor.  Each result is
+    the one gemm(a, b, out=out) gives, to the bit; the library runs them as one launch when they can share
+    it and one launch each otherwise.
+    """
+    if not problems:
+        return []
+    if len(problems) > GEMM_GROUP_MAX:
+        raise ValueError("at most %d problems per call" % GEMM_GROUP_MAX)
+    a0, _, out0 = problems[0]
+    grid = grid or a0.grid
+    kinds = {torch.float32: "f32", torch.bfloat16: "bf16"}
+    args = []
+    for i, (a, b, out) in enumerate(problems):
+        if a.k != a0.k or b.k != a0.k:
+            raise ValueError("problem %d: every operand must have K = %d" % (i, a0.k))
+        if a.block != a0.block or b.block != a0.block:
+            raise ValueError("problem %d: operands disagree on the block size" % i)
+        if out.dtype != out0.dtype:
+            raise ValueError("problem %d: every output must be %s" % (i, out0.dtype))
+        if out.dim() != 2 or out.shape[0] != a.lines or out.shape[1] != b.lines or out.stride(1) != 1:
+            raise ValueError("problem %d: out must be a row-major (%d, %d) view" % (i, a.lines, b.lines))
+        for name, q in (("a", a), ("b", b)):
+            if q.scales.shape[1] * q.block != q.k:
+                raise ValueError("problem %d, %s: %d scale bytes per line do not cover K = %d in blocks of %d"
+                                 % (i, name, q.scales.shape[1], q.k, q.block))
+        args.append((a.c_struct(), b.c_struct(), a.lines, b.lines, out.data_ptr(), out.stride(0)))
+    st = _lib.mx_gemm_grouped(args, a0.k, _lib.GRID[grid], a0.block, _lib.OUT[kinds[out0.dtype]],
+                              _stream(out0.device))
+    _lib.check(st, "mx_gemm_grouped")
+    return [out for _, _, out in problems]
 
 
 def mxnorm_quantize(x, power, c, grid="e2m1", rounding="rtne", seed=0, out=None, rho=None):

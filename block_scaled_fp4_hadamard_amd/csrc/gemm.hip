@@ -503,26 +503,69 @@ struct Walk {
   int xcd, member, rounds;
 };
 
-__device__ __forceinline__ bool round_tile(const TileMap& tm, const Walk& w, int r, int& bm, int& bn) {
-  const int g = r * kXcds + w.xcd;
-  if (g >= tm.groups) return false;
+// The problems one launch walks: one GEMM, or several that share K, the
+// operand pitches, the grid and the output kind (a grouped launch).  Their
+// tile groups are numbered one after the other, problem i holding groups
+// gend[i-1] .. gend[i]-1 (gend[-1] = 0; entries past the last problem repeat
+// its end), so a round deals groups of different problems to different XCDs
+// and a problem whose tiles end part-way through a round leaves no CU idle
+// while another problem has tiles left.
+template <int NP>
+struct GemmSet {
+  GemmParams p[NP];
+  TileMap tm[NP];
+  int gend[NP];
+};
+
+// element i of a per-problem array, i wave-uniform (a chain of scalar selects, no indexed load)
+template <typename T, int NP>
+__device__ __forceinline__ T pick(const T (&v)[NP], int i) {
+  T x = v[0];
+#pragma unroll
+  for (int j = 1; j < NP; ++j)
+    if (i == j) x = v[j];
+  return x;
+}
+
+template <int NP>
+__device__ __forceinline__ bool round_tile(const GemmSet<NP>& s, const Walk& w, int r, int& pi, int& bm, int& bn) {
+  int g = r * kXcds + w.xcd;
+  pi = 0;
+  if constexpr (NP == 1) {
+    if (g >= s.tm[0].groups) return false;
+  } else {
+    if (g >= s.gend[NP - 1]) return false;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NP - 1; ++i)
+      if (g >= s.gend[i]) {
+        pi = i + 1;
+        base = s.gend[i];
+      }
+    g -= base;
+  }
+  const TileMap tm = NP == 1 ? s.tm[0] : pick(s.tm, pi);
   bm = (g % tm.groups_m) * kGroupM + w.member % kGroupM;
   bn = (g / tm.groups_m) * kGroupN + w.member / kGroupM;
   return bm < tm.tiles_m && bn < tm.tiles_n;
 }
 
 // first round >= r holding a tile for this workgroup, or w.rounds
-__device__ __forceinline__ int next_round(const TileMap& tm, const Walk& w, int r, int& bm, int& bn) {
+template <int NP>
+__device__ __forceinline__ int next_round(const GemmSet<NP>& s, const Walk& w, int r, int& pi, int& bm, int& bn) {
   for (; r < w.rounds; ++r)
-    if (round_tile(tm, w, r, bm, bn)) return r;
+    if (round_tile(s, w, r, pi, bm, bn)) return r;
   return w.rounds;
 }
 
 // RK: K is not a multiple of 256 (a ragged last step); a separate instance, so
-// that the whole-step kernel carries none of its register cost
-template <int GRID, int OUT, bool RK, int NT, bool W16>
+// that the whole-step kernel carries none of its register cost.  NP: problems
+// in the launch (1, or a grouped launch's slots); K and the operand pitches are
+// the first problem's, which every problem of a grouped launch shares.
+template <int GRID, int OUT, bool RK, int NT, bool W16, int NP>
 __global__ void __launch_bounds__(full_threads<NT>(), 1)
-gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
+gemm_full_kernel(const GemmSet<NP> s, int rounds) {
+  const GemmParams& p = s.p[0];
   __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kFullStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kFullStageBytes];
   __shared__ __attribute__((aligned(1024))) uint32_t sSA[2][2 * kBM];    // [dword d][row]: blocks 4d..4d+3
@@ -532,8 +575,8 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   w.xcd = blockIdx.x % kXcds;
   w.member = blockIdx.x / kXcds;
   w.rounds = rounds;
-  int bm, bn;
-  int r = next_round(tm, w, 0, bm, bn);
+  int pi, bm, bn;
+  int r = next_round(s, w, 0, pi, bm, bn);
   if (r >= w.rounds) return;
 
   const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -572,14 +615,15 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
   const uint32_t lA = lds_addr(&sA[0][32 * (wave & 3) * kRowBytes]), lB = lds_addr(&sB[0][32 * (wave & 3) * kRowBytes]);
   const uint32_t lSA = lds_addr(&sSA[0][64 * (wave & 3)]), lSB = lds_addr(&sSB[0][64 * (wave & 3)]);
 
-  // DMA of K step kt of tile (tbm, tbn) into stage st, by the waves of parity kt % 2
-  auto issue = [&](int tbm, int tbn, int kt, int st) {
+  // DMA of K step kt of tile (tbm, tbn) of problem tpi into stage st, by the waves of parity kt % 2
+  auto issue = [&](int tpi, int tbm, int tbn, int kt, int st) {
     if (NT == 2 && (wave >> 2) != (kt & 1)) return;
-    const int64_t m0 = tile_origin(tbm, kBM, p.M), n0 = tile_origin(tbn, kBN, p.N);
-    const uint8_t* abase = wave_uniform(p.a_codes + m0 * p.lda_codes);
-    const uint8_t* bbase = wave_uniform(p.b_codes + n0 * p.ldb_codes);
-    const uint8_t* sabase = wave_uniform(p.a_scales + m0 * p.lda_scales);
-    const uint8_t* sbbase = wave_uniform(p.b_scales + n0 * p.ldb_scales);
+    const GemmParams& q = NP == 1 ? p : pick(s.p, tpi);
+    const int64_t m0 = tile_origin(tbm, kBM, q.M), n0 = tile_origin(tbn, kBN, q.N);
+    const uint8_t* abase = wave_uniform(q.a_codes + m0 * p.lda_codes);
+    const uint8_t* bbase = wave_uniform(q.b_codes + n0 * p.ldb_codes);
+    const uint8_t* sabase = wave_uniform(q.a_scales + m0 * p.lda_scales);
+    const uint8_t* sbbase = wave_uniform(q.b_scales + n0 * p.ldb_scales);
     const uint32_t kb = (uint32_t)kt * kRowBytes;
     const int vb = blocks_in(kt);
     if (vb == 8) {
@@ -635,16 +679,16 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   // the tile after the current one, and the DMA cursor two K steps ahead
-  int nbm = 0, nbn = 0;
-  int rn = next_round(tm, w, r + 1, nbm, nbn);
+  int npi = 0, nbm = 0, nbn = 0;
+  int rn = next_round(s, w, r + 1, npi, nbm, nbn);
   Frags<NT> f0, f1;
   const int shift = 8 * (lane >> 5);
-  issue(bm, bn, 0, 0);
+  issue(pi, bm, bn, 0, 0);
   // the waits and the barrier in one asm statement: its memory clobber keeps the compiler's LDS
   // accesses on their side of the barrier (the barrier builtin alone is not a memory operation)
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  if (nk > 1) issue(bm, bn, 1, 1);
-  else if (rn < w.rounds) issue(nbm, nbn, 0, 1);
+  if (nk > 1) issue(pi, bm, bn, 1, 1);
+  else if (rn < w.rounds) issue(npi, nbm, nbn, 0, 1);
   load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0), f1);
   int st = 0;
   for (;;) {
@@ -673,8 +717,8 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
         // the next step's stage has landed for this wave; every wave has read
         // its last fragments of this stage; then refill it two steps ahead
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kt + 2 < nk) issue(bm, bn, kt + 2, st);
-        else if (rn < w.rounds && kt + 2 - nk < nk) issue(nbm, nbn, kt + 2 - nk, st);
+        if (kt + 2 < nk) issue(pi, bm, bn, kt + 2, st);
+        else if (rn < w.rounds && kt + 2 - nk < nk) issue(npi, nbm, nbn, kt + 2 - nk, st);
         st ^= 1;
         load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0), f1);
       }
@@ -682,7 +726,12 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
       mfma_quarter<GRID, 2, NT>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_tile_wide<OUT, 4, NT, W16>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc);
+    if constexpr (NP == 1) {
+      store_tile_wide<OUT, 4, NT, W16>(p, tile_origin(bm, kBM, p.M) + r0, tile_origin(bn, kBN, p.N) + c0, lane, acc);
+    } else {
+      const GemmParams q = pick(s.p, pi);
+      store_tile_wide<OUT, 4, NT, W16>(q, tile_origin(bm, kBM, q.M) + r0, tile_origin(bn, kBN, q.N) + c0, lane, acc);
+    }
     if (rn >= w.rounds) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -691,9 +740,10 @@ gemm_full_kernel(const GemmParams p, const TileMap tm, int rounds) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
     r = rn;
+    pi = npi;
     bm = nbm;
     bn = nbn;
-    rn = next_round(tm, w, r + 1, nbm, nbn);
+    rn = next_round(s, w, r + 1, npi, nbm, nbn);
   }
 }
 
@@ -762,49 +812,106 @@ gemm_general_kernel(const GemmParams p, const TileMap tm) {
 // barrier and copy issue; on the Llama shapes they ran 5-18% slower, with the same output bits.
 constexpr int kWaveTileN = 2;
 
-template <int GRID, int OUT>
-static void launch_kind(const GemmParams& p, const TileMap& tm, bool full, dim3 g, hipStream_t s) {
-  if (full) {
-    // one workgroup per CU: 8 XCDs x 32 members; round r deals group r*8+xcd
-    const int rounds = (tm.groups + kXcds - 1) / kXcds;
-    constexpr int NT = kWaveTileN;
-    const dim3 g(kXcds * kGroupM * kGroupN), b(full_threads<NT>());
-    // bf16 rows written 16 bytes per lane need 16-byte aligned rows and tile origins
-    const bool wide16 = p.ldc % 8 == 0 && p.N % 8 == 0 && (uintptr_t)p.c % 16 == 0;
-    // (fp32 rows are always written 16 bytes per lane: one instance)
-    if constexpr (OUT == MX_OUT_F32) {
-      if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, true>), g, b, 0, s, p, tm, rounds);
-      else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, true>), g, b, 0, s, p, tm, rounds);
-    } else if (wide16) {
-      if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, true>), g, b, 0, s, p, tm, rounds);
-      else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, true>), g, b, 0, s, p, tm, rounds);
-    } else {
-      if (p.K % 256 == 0) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, false>), g, b, 0, s, p, tm, rounds);
-      else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, false>), g, b, 0, s, p, tm, rounds);
-    }
-  } else {
-    hipLaunchKernelGGL((gemm_general_kernel<GRID, OUT>), g, dim3(kGemmThreads), 0, s, p, tm);
+// whole-tile kernel instance for a grid, output kind, K and output row form
+template <int GRID, int OUT, int NP>
+static void launch_full(const GemmSet<NP>& set, int groups, bool wide16, hipStream_t s) {
+  // one workgroup per CU: 8 XCDs x 32 members; round r deals group r*8+xcd
+  const int rounds = (groups + kXcds - 1) / kXcds;
+  constexpr int NT = kWaveTileN;
+  const dim3 g(kXcds * kGroupM * kGroupN), b(full_threads<NT>());
+  const bool rk = set.p[0].K % 256 != 0;
+  // fp32 rows are always written 16 bytes per lane, bf16 rows when wide16 holds (a grouped launch is
+  // made only then)
+  constexpr bool kNarrow = OUT == MX_OUT_BF16 && NP == 1;
+  if (!kNarrow || wide16) {
+    if (!rk) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, true, NP>), g, b, 0, s, set, rounds);
+    else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, true, NP>), g, b, 0, s, set, rounds);
+  } else if constexpr (kNarrow) {
+    if (!rk) hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, false, NT, false, NP>), g, b, 0, s, set, rounds);
+    else hipLaunchKernelGGL((gemm_full_kernel<GRID, OUT, true, NT, false, NP>), g, b, 0, s, set, rounds);
   }
 }
 
-hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s) {
+static TileMap tile_map(const GemmParams& p) {
   TileMap tm;
   tm.tiles_m = (int)((p.M + kBM - 1) / kBM);
   tm.tiles_n = (int)((p.N + kBN - 1) / kBN);
   tm.groups_m = (tm.tiles_m + kGroupM - 1) / kGroupM;
   const int groups_n = (tm.tiles_n + kGroupN - 1) / kGroupN;
   tm.groups = tm.groups_m * groups_n;
-  const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
-  const dim3 g((unsigned)wgs);
-  const bool full = gemm_full_path(p.M, p.N, p.K, (uintptr_t)p.a_scales, (uintptr_t)p.b_scales, p.lda_codes,
-                                   p.ldb_codes, p.lda_scales, p.ldb_scales, (uintptr_t)p.c, p.ldc,
-                                   out_kind == MX_OUT_F32);
-  if (grid_kind == MX_GRID_E2M1) {
-    if (out_kind == MX_OUT_F32) launch_kind<MX_GRID_E2M1, MX_OUT_F32>(p, tm, full, g, s);
-    else launch_kind<MX_GRID_E2M1, MX_OUT_BF16>(p, tm, full, g, s);
+  return tm;
+}
+
+static bool full_path(const GemmParams& p, int out_kind) {
+  return gemm_full_path(p.M, p.N, p.K, (uintptr_t)p.a_scales, (uintptr_t)p.b_scales, p.lda_codes, p.ldb_codes,
+                        p.lda_scales, p.ldb_scales, (uintptr_t)p.c, p.ldc, out_kind == MX_OUT_F32);
+}
+
+// bf16 rows written 16 bytes per lane need 16-byte aligned rows and tile origins
+static bool wide16_rows(const GemmParams& p) {
+  return p.ldc % 8 == 0 && p.N % 8 == 0 && (uintptr_t)p.c % 16 == 0;
+}
+
+hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s) {
+  GemmSet<1> set;
+  set.p[0] = p;
+  set.tm[0] = tile_map(p);
+  set.gend[0] = set.tm[0].groups;
+  const TileMap& tm = set.tm[0];
+  if (full_path(p, out_kind)) {
+    const bool w16 = wide16_rows(p);
+    if (grid_kind == MX_GRID_E2M1) {
+      if (out_kind == MX_OUT_F32) launch_full<MX_GRID_E2M1, MX_OUT_F32>(set, tm.groups, w16, s);
+      else launch_full<MX_GRID_E2M1, MX_OUT_BF16>(set, tm.groups, w16, s);
+    } else {
+      if (out_kind == MX_OUT_F32) launch_full<MX_GRID_E1M2, MX_OUT_F32>(set, tm.groups, w16, s);
+      else launch_full<MX_GRID_E1M2, MX_OUT_BF16>(set, tm.groups, w16, s);
+    }
   } else {
-    if (out_kind == MX_OUT_F32) launch_kind<MX_GRID_E1M2, MX_OUT_F32>(p, tm, full, g, s);
-    else launch_kind<MX_GRID_E1M2, MX_OUT_BF16>(p, tm, full, g, s);
+    const int wgs = ((tm.groups + kXcds - 1) / kXcds) * kXcds * kGroupM * kGroupN;
+    const dim3 g((unsigned)wgs), b(kGemmThreads);
+    if (grid_kind == MX_GRID_E2M1) {
+      if (out_kind == MX_OUT_F32) hipLaunchKernelGGL((gemm_general_kernel<MX_GRID_E2M1, MX_OUT_F32>), g, b, 0, s, p, tm);
+      else hipLaunchKernelGGL((gemm_general_kernel<MX_GRID_E2M1, MX_OUT_BF16>), g, b, 0, s, p, tm);
+    } else {
+      if (out_kind == MX_OUT_F32) hipLaunchKernelGGL((gemm_general_kernel<MX_GRID_E1M2, MX_OUT_F32>), g, b, 0, s, p, tm);
+      else hipLaunchKernelGGL((gemm_general_kernel<MX_GRID_E1M2, MX_OUT_BF16>), g, b, 0, s, p, tm);
+    }
+  }
+  return hipGetLastError();
+}
+
+// Several GEMMs in one persistent launch when they all take the whole-tile path with one K, one set of
+// operand pitches and (bf16) 16-byte rows; otherwise each runs as its own launch, with the same results.
+hipError_t launch_gemm_grouped(const GemmParams* ps, int count, int grid_kind, int out_kind, hipStream_t s) {
+  bool together = count > 1 && count <= kMaxGroup;
+  for (int i = 0; together && i < count; ++i) {
+    const GemmParams& p = ps[i];
+    together = full_path(p, out_kind) && (out_kind == MX_OUT_F32 || wide16_rows(p)) && p.K == ps[0].K &&
+               p.lda_codes == ps[0].lda_codes && p.ldb_codes == ps[0].ldb_codes &&
+               p.lda_scales == ps[0].lda_scales && p.ldb_scales == ps[0].ldb_scales;
+  }
+  if (!together) {
+    for (int i = 0; i < count; ++i) {
+      const hipError_t e = launch_gemm(ps[i], grid_kind, out_kind, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GemmSet<kMaxGroup> set;
+  int groups = 0;
+  for (int i = 0; i < kMaxGroup; ++i) {
+    set.p[i] = ps[i < count ? i : count - 1];
+    set.tm[i] = tile_map(set.p[i]);
+    if (i < count) groups += set.tm[i].groups;
+    set.gend[i] = groups;
+  }
+  if (grid_kind == MX_GRID_E2M1) {
+    if (out_kind == MX_OUT_F32) launch_full<MX_GRID_E2M1, MX_OUT_F32>(set, groups, true, s);
+    else launch_full<MX_GRID_E2M1, MX_OUT_BF16>(set, groups, true, s);
+  } else {
+    if (out_kind == MX_OUT_F32) launch_full<MX_GRID_E1M2, MX_OUT_F32>(set, groups, true, s);
+    else launch_full<MX_GRID_E1M2, MX_OUT_BF16>(set, groups, true, s);
   }
   return hipGetLastError();
 }

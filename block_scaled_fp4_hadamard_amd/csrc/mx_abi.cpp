@@ -115,6 +115,39 @@ mx_status quantize_impl(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
   return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
 }
 
+// mx_gemm's argument checks; on MX_OK with M, N > 0, p holds the problem
+mx_status gemm_args(const mx_qtensor* a, const mx_qtensor* b, int64_t M, int64_t N, int64_t K, int grid,
+                    int32_t block, void* c, int64_t ldc, int out, mx::GemmParams& p) {
+  if (M < 0 || N < 0 || K <= 0) return MX_ERR_INVALID;
+  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
+  if (out != MX_OUT_F32 && out != MX_OUT_BF16) return MX_ERR_INVALID;
+  if (block != 16 && block != 32) return MX_ERR_INVALID;
+  if (K % block != 0) return MX_ERR_INVALID;
+  if (M == 0 || N == 0) return MX_OK;
+  mx_status s = check_qtensor(a, M, K, block);
+  if (s != MX_OK) return s;
+  s = check_qtensor(b, N, K, block);
+  if (s != MX_OK) return s;
+  const uintptr_t esize = out == MX_OUT_F32 ? 4u : 2u;
+  if (c == nullptr || ((uintptr_t)c % esize) != 0 || ldc < N) return MX_ERR_INVALID;
+  if (block != 32) return MX_ERR_UNSUPPORTED;
+  p = mx::GemmParams{};
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.b_codes = b->codes;
+  p.b_scales = b->scales;
+  p.lda_codes = a->ld_codes;
+  p.lda_scales = a->ld_scales;
+  p.ldb_codes = b->ld_codes;
+  p.ldb_scales = b->ld_scales;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.c = c;
+  p.ldc = ldc;
+  return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,34 +170,26 @@ mx_status mx_hadamard_quantize(const uint16_t* x, int64_t rows, int64_t cols, in
 
 mx_status mx_gemm(const mx_qtensor* a, const mx_qtensor* b, int64_t M, int64_t N, int64_t K, mx_grid grid,
                   int32_t block, void* c, int64_t ldc, mx_out out, void* hip_stream) {
-  if (M < 0 || N < 0 || K <= 0) return MX_ERR_INVALID;
-  if (grid != MX_GRID_E2M1 && grid != MX_GRID_E1M2) return MX_ERR_INVALID;
-  if (out != MX_OUT_F32 && out != MX_OUT_BF16) return MX_ERR_INVALID;
-  if (block != 16 && block != 32) return MX_ERR_INVALID;
-  if (K % block != 0) return MX_ERR_INVALID;
-  if (M == 0 || N == 0) return MX_OK;
-  mx_status s = check_qtensor(a, M, K, block);
-  if (s != MX_OK) return s;
-  s = check_qtensor(b, N, K, block);
-  if (s != MX_OK) return s;
-  const uintptr_t esize = out == MX_OUT_F32 ? 4u : 2u;
-  if (c == nullptr || ((uintptr_t)c % esize) != 0 || ldc < N) return MX_ERR_INVALID;
-  if (block != 32) return MX_ERR_UNSUPPORTED;
   mx::GemmParams p{};
-  p.a_codes = a->codes;
-  p.a_scales = a->scales;
-  p.b_codes = b->codes;
-  p.b_scales = b->scales;
-  p.lda_codes = a->ld_codes;
-  p.lda_scales = a->ld_scales;
-  p.ldb_codes = b->ld_codes;
-  p.ldb_scales = b->ld_scales;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.c = c;
-  p.ldc = ldc;
+  const mx_status s = gemm_args(a, b, M, N, K, grid, block, c, ldc, out, p);
+  if (s != MX_OK || M == 0 || N == 0) return s;
   hipError_t e = mx::launch_gemm(p, grid, out, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
+}
+
+mx_status mx_gemm_grouped(const mx_gemm_problem* problems, int32_t count, int64_t K, mx_grid grid, int32_t block,
+                          mx_out out, void* hip_stream) {
+  if (problems == nullptr || count < 1 || count > MX_GEMM_GROUP_MAX) return MX_ERR_INVALID;
+  mx::GemmParams ps[MX_GEMM_GROUP_MAX];
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const mx_gemm_problem& q = problems[i];
+    const mx_status s = gemm_args(q.a, q.b, q.M, q.N, K, grid, block, q.c, q.ldc, out, ps[n]);
+    if (s != MX_OK) return s;
+    if (q.M > 0 && q.N > 0) ++n;
+  }
+  if (n == 0) return MX_OK;
+  hipError_t e = mx::launch_gemm_grouped(ps, n, grid, out, (hipStream_t)hip_stream);
   return e == hipSuccess ? MX_OK : MX_ERR_DEVICE;
 }
 

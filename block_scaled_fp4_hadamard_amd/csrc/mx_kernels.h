@@ -85,6 +85,9 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm(const GemmParams& p, int grid_kind, int out_kind, hipStream_t s);
+// up to kMaxGroup GEMMs of one K: one launch when they can share it, else one launch each
+constexpr int kMaxGroup = MX_GEMM_GROUP_MAX;
+hipError_t launch_gemm_grouped(const GemmParams* ps, int count, int grid_kind, int out_kind, hipStream_t s);
 
 struct MxNormParams {
   const uint16_t* x;

@@ -23,6 +23,14 @@ stochastic rounding on dY only, round-to-nearest-even elsewhere.  Both
 operands of a GEMM are rotated along its contraction axis with the same sign
 vector, so the rotation cancels in the product; one had_seed serves the block.
 
+Nothing in the backward pass reads dW before the optimizer step, so Wgrads may
+run late and together.  The whole-tile GEMM runs 256 persistent workgroups,
+one 256 x 256 tile each per round, and a Wgrad whose tile count is not a
+multiple of 256 leaves part of its last round idle.  When two or more do, they
+are deferred to the end of the step and run as one grouped launch
+(mx_gemm_grouped), whose rounds deal tiles of all of them; each result is the
+one its own launch gives, to the bit.
+
 This module only sequences library calls; every step runs in the HIP kernels.
 """
 from dataclasses import dataclass, field
@@ -54,6 +62,15 @@ class Launch:
     fn: object            # zero-argument callable that enqueues the launch
     bytes: int = 0        # algorithmic HBM bytes
     flops: int = 0
+    gemms: int = 0        # GEMM products the launch computes
+
+
+GEMM_TILE = 256           # rows and columns of C per whole-tile workgroup
+GEMM_ROUND_TILES = 256    # tiles per round of the persistent whole-tile grid
+
+
+def gemm_tiles(m, n):
+    return -(-m // GEMM_TILE) * -(-n // GEMM_TILE)
 
 
 @dataclass
@@ -65,6 +82,7 @@ class Recipe:
     sr_on_dy: bool = True
     sr_seed_base: int = 5000
     fuse: bool = True          # q/k/v and gate/up as fused projections
+    group_wgrad: bool = True   # Wgrads that leave the last GEMM round part-empty run grouped at the end
 
 
 def quant_bytes(rows, cols, axes=2):
@@ -74,7 +92,7 @@ def quant_bytes(rows, cols, axes=2):
 
 @dataclass
 class LlamaBlockStep:
-    """All quantizations and the 21 GEMMs of one Llama block's seven linears.
+    """All quantizations and the 21 GEMM products of one Llama block's seven linears.
 
     tensors: dict of int16 CUDA tensors keyed like synth.llama_block().
     """
@@ -114,6 +132,11 @@ class LlamaBlockStep:
             quant[name] = Launch("quant." + rounding, "quantize " + name, fn, quant_bytes(rows, cols))
         # each projection's quantizations run just before its three GEMMs, as in a training step: the
         # quantized operands are then still in the last-level cache when the GEMMs read them
+        partial = [name for name, parts in proj.items()
+                   if gemm_tiles(sum(LLAMA_LINEARS[p][0] for p in parts), LLAMA_LINEARS[parts[0]][1])
+                   % GEMM_ROUND_TILES]
+        deferred = partial if r.group_wgrad and len(partial) > 1 else []
+        wgrads = []
         done = set()
         for name, parts in proj.items():
             for tname in (LLAMA_INPUT_OF[parts[0]], "w_" + name, "dy_" + name):
@@ -129,15 +152,28 @@ class LlamaBlockStep:
             self.out[name] = {"y": y, "dx": dx, "dw": dw}
             flops = 2 * tokens * o * i
             self.launches.append(Launch("gemm.bf16", "fprop " + name,
-                                        lambda a=xq["row"], b=wq["row"], c=y: api.gemm(a, b, out=c), 0, flops))
+                                        lambda a=xq["row"], b=wq["row"], c=y: api.gemm(a, b, out=c), 0, flops, 1))
             self.launches.append(Launch("gemm.bf16", "dgrad " + name,
-                                        lambda a=dq["row"], b=wq["col"], c=dx: api.gemm(a, b, out=c), 0, flops))
-            self.launches.append(Launch("gemm.f32", "wgrad " + name,
-                                        lambda a=dq["col"], b=xq["col"], c=dw: api.gemm(a, b, out=c), 0, flops))
+                                        lambda a=dq["row"], b=wq["col"], c=dx: api.gemm(a, b, out=c), 0, flops, 1))
+            if name in deferred:
+                wgrads.append((name, (dq["col"], xq["col"], dw), flops))
+            else:
+                self.launches.append(Launch("gemm.f32", "wgrad " + name,
+                                            lambda a=dq["col"], b=xq["col"], c=dw: api.gemm(a, b, out=c), 0,
+                                            flops, 1))
+        for at in range(0, len(wgrads), api.GEMM_GROUP_MAX):
+            chunk = wgrads[at:at + api.GEMM_GROUP_MAX]
+            self.launches.append(Launch("gemm.f32", "wgrad " + " + ".join(n for n, _, _ in chunk),
+                                        lambda probs=[p for _, p, _ in chunk]: api.gemm_grouped(probs), 0,
+                                        sum(f for _, _, f in chunk), len(chunk)))
 
     def run(self):
         for L in self.launches:
             L.fn()
+
+    @property
+    def gemms(self):
+        return sum(L.gemms for L in self.launches)
 
     @property
     def flops(self):

@@ -169,6 +169,38 @@ mx_status mx_gemm(const mx_qtensor *a, const mx_qtensor *b, int64_t M, int64_t N
                   void *hip_stream);
 
 /*
+ * mx_gemm_grouped: count independent mx_gemm problems of one K, grid and
+ * output kind in one launch ("Pre-addestramento ... con MXFP4", Metodologia:
+ * the Wgrad GEMMs of a block's linear layers, which nothing in the backward
+ * pass reads before the optimizer step, so they can run as a group).  Problem
+ * i computes C_i[m][n] = sum_k A_i[m][k] * B_i[n][k] exactly as mx_gemm(a_i,
+ * b_i, M_i, N_i, K, grid, block, c_i, ldc_i, out) does, to the bit.  One
+ * persistent launch walks the tiles of all problems when every problem takes
+ * mx_gemm's fast path, the problems share the operand pitches (ld_codes and
+ * ld_scales of every a_i, and of every b_i), and bf16 outputs have
+ * ldc_i % 8 == 0, N_i % 8 == 0 and 16-byte aligned c_i; a problem whose tiles
+ * end part-way through a round of the chip then leaves no CU idle while the
+ * next problem has tiles.  Otherwise the problems run one launch each, in
+ * order.  The outputs must not overlap one another or any operand.
+ *   problems   host array of count entries (read before the call returns)
+ *   count      1 .. MX_GEMM_GROUP_MAX
+ *   K, grid, block, out   as mx_gemm, for every problem
+ * Every problem is validated as mx_gemm validates its arguments before
+ * anything is launched; problems with M_i or N_i of 0 are skipped.
+ */
+#define MX_GEMM_GROUP_MAX 8
+typedef struct {
+    const mx_qtensor *a;   /* M lines of length K */
+    const mx_qtensor *b;   /* N lines of length K */
+    int64_t M, N;
+    void *c;               /* device, row-major [M][ldc] */
+    int64_t ldc;
+} mx_gemm_problem;
+
+mx_status mx_gemm_grouped(const mx_gemm_problem *problems, int32_t count, int64_t K, mx_grid grid,
+                          int32_t block, mx_out out, void *hip_stream);
+
+/*
  * mx_mxnorm_quantize: MXNorm fused with the row-wise MX cast ("MXNorm: Reusing
  * MXFP block scales for efficient tensor normalisation", Sommario tecnico 2).
  * Row t is scaled by rho_t = c * ((1/K) sum_k m_tk^p)^(-1/p), the inverse-RMS

@@ -106,6 +106,35 @@ def test_gemm_validation(kw, want):
     assert gemm(**kw) == want
 
 
+def grouped(problems, K=128, grid=0, block=32, out=0):
+    """problems: list of dicts of gemm()'s per-problem keywords (M, N, c, ldc, a, b)."""
+    args = []
+    for kw in problems:
+        d = dict(M=64, N=64, c=FAKE, ldc=64, a=q(ld_codes=64, ld_scales=4), b=q(ld_codes=64, ld_scales=4))
+        d.update(kw)
+        args.append((d["a"], d["b"], d["M"], d["N"], d["c"], d["ldc"]))
+    return _lib.mx_gemm_grouped(args, K, grid, block, out, None)
+
+
+@pytest.mark.parametrize("problems,kw,want", [
+    ([], {}, 1),                                            # count 0
+    ([dict(M=0)] * 9, {}, 1),                                # count above MX_GEMM_GROUP_MAX
+    ([dict(), dict()], dict(K=100), 1), ([dict()], dict(grid=3), 1), ([dict()], dict(out=2), 1),
+    ([dict(), dict(c=0)], {}, 1),                           # one bad problem: nothing runs
+    ([dict(c=0), dict()], {}, 1),
+    ([dict(), dict(ldc=60)], {}, 1), ([dict(a=q(ld_codes=32)), dict()], {}, 1),
+    ([dict(M=-1)], {}, 1),
+    ([dict(a=q(ld_scales=8), b=q(ld_scales=8))], dict(block=16), 2),
+    ([dict(M=0), dict(N=0)], {}, 0),                        # all empty: nothing to do
+])
+def test_gemm_grouped_validation(problems, kw, want):
+    assert grouped(problems, **kw) == want
+
+
+def test_gemm_grouped_rejects_a_null_array():
+    assert _lib.lib().mx_gemm_grouped(None, 1, 128, 0, 32, 0, None) == 1
+
+
 def mxnorm(x=FAKE, rows=8, cols=128, ld=128, power=2, c=2.39, grid=0, rnd=0, out="d", rho=FAKE):
     out = q() if out == "d" else out
     return _lib.mx_mxnorm_quantize(x, rows, cols, ld, power, c, grid, rnd, 0, out, rho, None)
