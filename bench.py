@@ -26,8 +26,8 @@ Prints one JSON line.  `value` is the step's GEMM work over its wall time
 (TFLOP/s, quantization included); `kernels` splits the time by kernel family
 with each family's achieved HBM GB/s or MFMA TFLOP/s; `step_e1m2` is the same
 step on the uniform grid; `workloads` times the quantizer-only workload (cold
-and hot, RTNE and SR), the fused-QKV Fprop GEMM and the MLP Dgrad and Wgrad
-GEMMs on their own; `mxnorm` times the fused MXNorm + row-wise cast launch,
+and hot, RTNE and SR, the rotation ablation and the diagnostics kernel), the
+fused-QKV Fprop GEMM and the MLP Dgrad and Wgrad GEMMs on their own; `mxnorm` times the fused MXNorm + row-wise cast launch,
 `nvfp4` the double-block quantizer; `mfma_ceiling` the FP4 MFMA's rate on
 register-resident zero, constant and random operands; `roofline` is the dominant kernel's;
 `cpu_baseline` is the CPU oracle on bounded samples.
@@ -474,8 +474,10 @@ def measure_quantizer(x, dev, stream):
     nbytes = rows * cols * 2 + 2 * (rows * cols // 2 + rows * cols // 32)
     xs = [x] + [x.clone() for _ in range(copies_for(x.numel() * 2) - 1)]
     q = {}
+    outs = {}
     for rounding, seed in (("rtne", 0), ("sr", 1)):
         sets = [(api.empty_qtensor(rows, cols, dev), api.empty_qtensor(cols, rows, dev)) for _ in xs]
+        outs[rounding] = sets
 
         def run(i, rounding=rounding, seed=seed, sets=sets, n=len(xs)):
             api.quantize(xs[i % n], axis="both", rounding=rounding, seed=seed, had_n=32, had_kind="det",
@@ -490,7 +492,31 @@ def measure_quantizer(x, dev, stream):
                bytes_per_call=nbytes, timing="median of 64 calls; cold: %d input and output sets in rotation "
                "(%.2f GB of input)" % (len(xs), len(xs) * x.numel() * 2 / 1e9), **q)
     out["rotation_ablation"] = measure_ablation(xs, sets, stream)
+    out["diagnostics"] = measure_diag(xs, outs["rtne"], stream)
     return out
+
+
+def measure_diag(xs, sets, stream):
+    """The quantization diagnostics kernel (signal and noise energy, code histogram) on the quantizer-only
+    workload's RTNE outputs, each axis its own launch, H32 recomputed from the bf16 input, the same tensors in
+    rotation.  Algorithmic bytes per launch: the bf16 read and the output's codes and scales (2.53125 B per
+    element); the twelve float64 totals stay on the device between launches."""
+    import torch
+    from block_scaled_fp4_hadamard_amd import api
+    n = len(xs)
+    rows, cols = xs[0].shape
+    nbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 32
+    buf = torch.zeros(12, dtype=torch.float64, device=xs[0].device)
+    res = {"workload": "SQNR and code histogram of the H32 RTNE outputs of X %dx%d, each axis its own launch"
+                       % (rows, cols), "bytes_per_launch": nbytes, "timing": "median of 50 launches"}
+    for ax, k in (("row", 0), ("col", 1)):
+        def run(i, ax=ax, k=k):
+            api.quant_stats(xs[i % n], sets[i % n][k], axis=ax, had_n=32, had_kind="det", stats=buf, to_host=False)
+        run(0)
+        us = time_median_us(run, 50, stream)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[ax] = {"us_per_launch": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def measure_ablation(xs, sets, stream):

@@ -180,10 +180,12 @@ def mxnorm_quantize(x, power, c, grid="e2m1", rounding="rtne", seed=0, out=None,
     return q, r
 
 
-def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0, stats=None):
+def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0, stats=None, to_host=True):
     """Diagnostic totals of one quantized output q of x, as the kernel accumulates them: sum of y^2, sum of
     (y - y_hat)^2, the counts of the 8 magnitude codes and the number of blocks.  stats: an optional zeroed
     float64 (12,) CUDA tensor to reuse.  Ratios built from these (SQNR, bucket usage) are the caller's.
+    to_host=False returns the stats tensor itself, with no copy to the host and no synchronization (the
+    kernel adds to it: zero it before a call whose totals are read).
     """
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
@@ -195,6 +197,8 @@ def quant_stats(x, q, axis="row", grid=None, had_n=0, had_kind="det", had_seed=0
                              had_n, _lib.HAD["none" if not had_n else had_kind], had_seed, q.c_struct(),
                              buf.data_ptr(), _stream(x.device))
     _lib.check(st, "mx_quant_stats")
+    if not to_host:
+        return buf
     host = buf.cpu()
     counts = host[2:].view(torch.int64)
     return {"sum_sq": float(host[0]), "sum_err_sq": float(host[1]), "hist": [int(v) for v in counts[:8]],
