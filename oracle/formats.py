@@ -10,8 +10,8 @@ Sources, by page title and section:
 * "MXNorm: Reusing MXFP block scales ...", Sommario tecnico 2: each block gets
   one shared scale derived from its absolute maximum.
 The block size 32, the E8M0 scale byte and the rule
-scale = 2^(floor(log2 amax) - emax) are the MX layout the task statement fixes;
-the pages only imply them.
+scale = 2^(floor(log2 amax) - emax) are the OCP MX layout, which the pages use
+by name without spelling it out.
 """
 import math
 
@@ -21,7 +21,7 @@ E2M1 = "e2m1"
 E1M2 = "e1m2"
 GRIDS = (E2M1, E1M2)
 
-# The E2M1 magnitudes listed in the statement of the problem, by 3-bit code.
+# The E2M1 magnitudes (two exponent bits, one mantissa bit), by 3-bit code.
 E2M1_LEVELS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 # The uniform grid: code k is k/4 (E1M2 with exponent bias 1, or a
 # sign-magnitude INT4 scaled by 1/4).

@@ -25,7 +25,7 @@ def _quantize_lines(path, axis, start, stop, kw):
 
 
 def workers():
-    """Worker count: the machine's cores up to 12 (a GPU machine gives one process 16 cores)."""
+    """Worker count: the machine's cores up to 12 (some hosts give one process only 16 of their cores)."""
     return max(1, min(12, os.cpu_count() or 1))
 
 
