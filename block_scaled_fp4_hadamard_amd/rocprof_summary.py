@@ -13,7 +13,7 @@
 Kernel families: quant.rtne / quant.sr (the quantizer by rounding mode), gemm.bf16 / gemm.f32 (the GEMM by
 output type), mxnorm (the fused MXNorm cast), nvfp4.row / nvfp4.col and mx16.row /
 mx16.col (the 16-value block quantizers by axis), rotate and quant.f32 (the unfused rotation and cast),
-osci (OsciReset), probe.mfma and probe.valu (the rate probes), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
+osci (OsciReset), diag (the quantization diagnostics), probe.mfma and probe.valu (the rate probes), copy (the runtime's buffer copy).  The traffic file records a hash of the kernel sources so a
 reader can tell when the figures no longer describe the code.
 """
 import argparse
@@ -26,7 +26,8 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("quant.hip", "gemm.hip", "mxnorm.hip", "nvfp4.hip", "osci.hip", "mx_device.h", "mx_kernels.h")
+KERNEL_SOURCES = ("quant.hip", "gemm.hip", "mxnorm.hip", "nvfp4.hip", "osci.hip", "diag.hip", "mx_device.h",
+                  "mx_kernels.h")
 
 
 def sources_hash():
@@ -52,6 +53,8 @@ def kernel_family(name):
         return "quant.f32"
     if "osci_kernel" in name:
         return "osci"
+    if "quant_stats_kernel" in name:
+        return "diag"
     if "mfma_rate_kernel" in name:
         return "probe.mfma"
     if "valu_rate_kernel" in name:

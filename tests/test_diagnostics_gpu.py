@@ -39,3 +39,22 @@ def test_stats_match_the_oracle(axis, grid, had_n, had_kind):
         assert got["blocks"] == blocks and got["hist"] == hist.tolist()
         assert got["sum_sq"] == pytest.approx(s2, rel=1e-9)
         assert got["sum_err_sq"] == pytest.approx(e2, rel=1e-9)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_stats_persistent_walk(axis):
+    """3104 x 4160 (97 x 130 blocks of 32): 403,520 blocks on either axis for the persistent grid's
+    262,144 lanes, so lanes take one or two blocks and the (line, block) cursor carries across lines at a
+    stride that does not divide the line count.  H32 deterministic, E2M1 RTNE."""
+    announce("quant stats persistent walk %s 3104x4160 H32" % axis)
+    rng = np.random.default_rng(67)
+    bits = synth.activation(3104, 4160, rng)
+    x = to_gpu_bits(bits)
+    q = quantize(x, axis=axis, had_n=32, had_kind="det")[axis]
+    got = quant_stats(x, q, axis, "e2m1", 32, "det", 0)
+    torch.cuda.synchronize()
+    codes, scales = qt_to_np(q)
+    s2, e2, hist, blocks = quant_stats_ref(bits, codes, scales, axis, "e2m1", 32, "det", 0)
+    assert got["blocks"] == blocks == 403520 and got["hist"] == hist.tolist()
+    assert got["sum_sq"] == pytest.approx(s2, rel=1e-9)
+    assert got["sum_err_sq"] == pytest.approx(e2, rel=1e-9)

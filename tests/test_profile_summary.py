@@ -21,7 +21,8 @@ def test_kernel_families():
         "void mx::mxnorm_kernel<0, 0, 2>(mx::MxNormParams)": "mxnorm",
         "void mx::block16_kernel<1, 0, 0, true>(mx::Block16Params, long)": "nvfp4.col",
         "void mx::block16_kernel<0, 1, 1, false>(mx::Block16Params, long)": "mx16.row",
-        "void mx::quant_stats_kernel<32>(mx::QuantStatsParams)": None,
+        "void mx::quant_stats_kernel<32, 0, false, true>(mx::QuantStatsParams)": "diag",
+        "void mx::rotate_kernel<32>(mx::RotateParams)": "rotate",
     }
     for name, fam in cases.items():
         assert kernel_family(name) == fam, name
