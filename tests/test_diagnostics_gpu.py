@@ -58,3 +58,25 @@ def test_stats_persistent_walk(axis):
     assert got["blocks"] == blocks == 403520 and got["hist"] == hist.tolist()
     assert got["sum_sq"] == pytest.approx(s2, rel=1e-9)
     assert got["sum_err_sq"] == pytest.approx(e2, rel=1e-9)
+
+
+@pytest.mark.parametrize("had_n", [0, 32])
+def test_stats_on_a_strided_unaligned_view(had_n):
+    """Row-wise statistics read from a view whose rows start 8 bytes off a 16-byte boundary (the kernel's
+    2-byte load path instead of its 16-byte one), with the pitch of a wider tensor."""
+    announce("quant stats strided view H%d" % had_n)
+    rng = np.random.default_rng(71)
+    bits = synth.activation(160, 320, rng)
+    full = np.zeros((160, 336), dtype=np.uint16)
+    full[:, 4:324] = bits
+    xf = to_gpu_bits(full)
+    x = xf[:, 4:324]
+    assert x.data_ptr() % 16 == 8
+    q = quantize(x.contiguous(), axis="row", had_n=had_n, had_kind="det")["row"]
+    got = quant_stats(x, q, "row", "e2m1", had_n, "det", 0)
+    torch.cuda.synchronize()
+    codes, scales = qt_to_np(q)
+    s2, e2, hist, blocks = quant_stats_ref(bits, codes, scales, "row", "e2m1", had_n, "det", 0)
+    assert got["blocks"] == blocks and got["hist"] == hist.tolist()
+    assert got["sum_sq"] == pytest.approx(s2, rel=1e-9)
+    assert got["sum_err_sq"] == pytest.approx(e2, rel=1e-9)
