@@ -259,3 +259,39 @@ def test_whole_tile_path_more_tiles_than_workgroups_full_output():
     c = run_gemm(a, b, "e2m1")
     c_ref, g = gemm_ref(*a, *b, k, "e2m1")
     assert_gemm_close(c, c_ref, g, "288 tiles")
+
+
+def scale_pitch(nb):
+    """A scale row pitch 8 to 11 bytes wider than nb and a multiple of 4 (what the whole-tile kernel needs)."""
+    return (nb + 3) // 4 * 4 + 8
+
+
+def pitched_qtensor(op, grid, extra_codes=48):
+    """A GPU operand whose code and scale rows sit in wider buffers (row pitches K/2 + extra_codes and
+    scale_pitch(K/32) bytes), the bytes past each row's end set to 0xFF: codes of -6 and NaN scales, so
+    that reading any of them would show in the products."""
+    codes, scales = op
+    lines, kb = codes.shape
+    nb = scales.shape[1]
+    cbuf = torch.full((lines, kb + extra_codes), 0xFF, dtype=torch.uint8)
+    cbuf[:, :kb] = torch.from_numpy(codes)
+    sbuf = torch.full((lines, scale_pitch(nb)), 0xFF, dtype=torch.uint8)
+    sbuf[:, :nb] = torch.from_numpy(scales)
+    return QTensor(cbuf.cuda()[:, :kb], sbuf.cuda()[:, :nb], grid)
+
+
+@pytest.mark.parametrize("grid", ["e2m1", "e1m2"])
+@pytest.mark.parametrize("m,n,k", [(512, 768, 1024), (640, 512, 1248), (300, 200, 160)])
+def test_operands_with_wider_row_pitches(grid, m, n, k):
+    """Operands read through row pitches wider than their rows (whole-tile kernel, its ragged-K form and
+    the bounds-checked kernel), the bytes between rows poisoned: fp32 output against the oracle."""
+    announce("gemm pitched operands %s %dx%dx%d" % (grid, m, n, k))
+    rng = np.random.default_rng(m + 5 * n + 11 * k)
+    a = random_operand(rng, m, k)
+    b = random_operand(rng, n, k)
+    qa, qb = pitched_qtensor(a, grid), pitched_qtensor(b, grid)
+    assert qa.codes.stride(0) == k // 2 + 48 and qa.scales.stride(0) == scale_pitch(k // 32)
+    c = gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c_ref, g = gemm_ref(*a, *b, k, grid)
+    assert_gemm_close(c.cpu().numpy(), c_ref, g, "pitched %s %dx%dx%d" % (grid, m, n, k))
