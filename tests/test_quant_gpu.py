@@ -173,3 +173,42 @@ def test_quantizer_workload_full_size(rounding, seed):
     """8192 x 4096 activations with 0.1% outlier channels, H32, both outputs: every byte."""
     bits = synth.quant_x()
     check(bits, "quant-full", axis="both", rounding=rounding, seed=seed, had_n=32, had_kind="det")
+
+
+def pitched_output(lines, k, grid, extra_codes=32, extra_scales=8, fill=0xA5):
+    """An output operand in wider buffers (row pitches k/2 + extra_codes and k/32 + extra_scales bytes), every
+    byte preset to `fill`; returns (QTensor, code buffer, scale buffer)."""
+    from block_scaled_fp4_hadamard_amd import QTensor
+    cbuf = torch.full((lines, k // 2 + extra_codes), fill, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((lines, k // 32 + extra_scales), fill, dtype=torch.uint8, device="cuda")
+    return QTensor(cbuf[:, :k // 2], sbuf[:, :k // 32], grid), cbuf, sbuf
+
+
+@pytest.mark.parametrize("rows,cols", [(96, 544), (256, 512)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_strided_input_and_pitched_outputs(rows, cols, rounding):
+    """The input read through a row pitch 64 elements wider than its rows, both outputs written through
+    code and scale pitches wider than theirs: the codes and scales equal the oracle's and every byte
+    between the output rows keeps its preset value.  256 x 512 takes the interior-tile store path (8-byte
+    aligned scale rows), 96 x 544 the bounds-checked one.  Random-sign H32, E2M1."""
+    announce("quantize strided input, pitched outputs %dx%d %s" % (rows, cols, rounding))
+    rng = np.random.default_rng(rows + cols)
+    bits = synth.activation(rows, cols, rng)
+    wide = np.zeros((rows, cols + 64), dtype=np.uint16)
+    wide[:, :cols] = bits
+    x = to_gpu_bits(wide)[:, :cols]
+    assert x.stride(0) == cols + 64
+    ro, rc, rs = pitched_output(rows, cols, "e2m1")
+    co, cc, cs = pitched_output(cols, rows, "e2m1")
+    kw = dict(axis="both", rounding=rounding, seed=21, had_n=32, had_kind="rand", had_seed=77)
+    out = quantize(x, row_out=ro, col_out=co, **kw)
+    torch.cuda.synchronize()
+    ref = quantize_ref(bits, **kw)
+    for key, (q, cbuf, sbuf) in (("row", (ro, rc, rs)), ("col", (co, cc, cs))):
+        assert out[key] is q
+        gc, gs = qt_to_np(q)
+        assert_bytes_equal(gs, ref[key][1], "pitched %s scales" % key)
+        assert_bytes_equal(gc, ref[key][0], "pitched %s codes" % key)
+        kb, nb = q.codes.shape[1], q.scales.shape[1]
+        assert np.all(cbuf.cpu().numpy()[:, kb:] == 0xA5), key + " code padding written"
+        assert np.all(sbuf.cpu().numpy()[:, nb:] == 0xA5), key + " scale padding written"
