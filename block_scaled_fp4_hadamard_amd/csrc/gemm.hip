@@ -116,6 +116,19 @@ __device__ __forceinline__ v8i operand(const uint4& x) {
   }
 }
 
+// The whole-tile kernel's operand: its E1M2 fragments already hold half of each block (load_quarter), so
+// the FP8 bytes need no exchange across the wave's halves.
+template <int GRID>
+__device__ __forceinline__ v8i operand_tile(const uint4& x) {
+  if constexpr (GRID == MX_GRID_E1M2 && kE1M2AsFp8) {
+    uint32_t o8[8];
+    e1m2_to_e4m3({x.x, x.y, x.z, x.w}, o8);
+    return v8i{(int)o8[0], (int)o8[1], (int)o8[2], (int)o8[3], (int)o8[4], (int)o8[5], (int)o8[6], (int)o8[7]};
+  } else {
+    return operand<GRID>(x);
+  }
+}
+
 // MFMA format code of a grid's operands: 4 fp4 E2M1; 0 fp8 E4M3 or 2 fp6 E2M3 for E1M2
 template <int GRID>
 constexpr int mfma_fmt() { return GRID == MX_GRID_E2M1 ? 4 : (kE1M2AsFp8 ? 0 : 2); }
@@ -423,21 +436,35 @@ struct Frags {
 // step).  A lane's block in quarter q is 2q + half; past the edge its codes
 // are zeros in LDS and its scale dwords may be stale or never copied, so it
 // takes a stand-in scale (all bytes 127): the products stay exact zeros.
-template <int NT>
+//
+// E1M2 (the 8-bit operand layout): lane l takes half of each of the quarter's two blocks instead of one
+// whole block, the 8 bytes at 8 * (l / 32) in both blocks' pieces, so that its converted bytes 0-15
+// belong to the first block and 16-31 to the second with no exchange across the wave's halves.
+template <int NT, int GRID>
 __device__ __forceinline__ void load_quarter(Frags<NT>& f, const uint8_t* a, const uint8_t* b, const uint32_t* sa,
                                              const uint32_t* sb, int q, int r0, int c0, int lane, int vb,
                                              const Frags<NT>& prev) {
   const int half = lane >> 5, lrow = lane & 31;
   const int off = lrow * kRowBytes + swz8(lrow, 2 * q + half);
+  const int off0 = lrow * kRowBytes + swz8(lrow, 2 * q) + 8 * half;
+  const int off1 = lrow * kRowBytes + swz8(lrow, 2 * q + 1) + 8 * half;
+  auto piece = [&](const uint8_t* base) {
+    if constexpr (GRID == MX_GRID_E1M2 && kE1M2AsFp8) {
+      const uint2 p0 = *(const uint2*)(base + off0), p1 = *(const uint2*)(base + off1);
+      return uint4{p0.x, p0.y, p1.x, p1.y};
+    } else {
+      return *(const uint4*)(base + off);
+    }
+  };
   // quarters 1 and 3 use the same scale dword as 0 and 2: taken from the previous quarter's fragments
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f.a[i] = *(const uint4*)(a + (r0 + 32 * i) * kRowBytes + off);
+    f.a[i] = piece(a + (r0 + 32 * i) * kRowBytes);
     f.sa[i] = (q & 1) ? prev.sa[i] : sa[(q >> 1) * kBM + r0 + 32 * i + lrow];
   }
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    f.b[j] = *(const uint4*)(b + (c0 + 32 * j) * kRowBytes + off);
+    f.b[j] = piece(b + (c0 + 32 * j) * kRowBytes);
     f.sb[j] = (q & 1) ? prev.sb[j] : sb[(q >> 1) * kBN + c0 + 32 * j + lrow];
   }
   if (vb < 8) {
@@ -461,12 +488,12 @@ __device__ __forceinline__ void mfma_quarter(const Frags<NT>& f, v16f (&acc)[4][
   int sbj[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    bj[j] = operand<GRID>(f.b[j]);
+    bj[j] = operand_tile<GRID>(f.b[j]);
     sbj[j] = (int)(f.sb[j] >> shift);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const v8i ai = operand<GRID>(f.a[i]);
+    const v8i ai = operand_tile<GRID>(f.a[i]);
     const int sai = (int)(f.sa[i] >> shift);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -689,7 +716,7 @@ gemm_full_kernel(const GemmSet<NP> s, int rounds) {
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   if (nk > 1) issue(pi, bm, bn, 1, 1);
   else if (rn < w.rounds) issue(npi, nbm, nbn, 0, 1);
-  load_quarter(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0), f1);
+  load_quarter<NT, GRID>(f0, sA[0], sB[0], sSA[0], sSB[0], 0, r0, c0, lane, blocks_in(0), f1);
   int st = 0;
   for (;;) {
     for (int kt = 0; kt < nk; ++kt) {
@@ -700,15 +727,15 @@ gemm_full_kernel(const GemmSet<NP> s, int rounds) {
       // sched_barrier keeps each phase where it is written: without it the
       // scheduler hoists every quarter's reads to the top and runs out of VGPRs
       const int vb = blocks_in(kt);
-      load_quarter(f1, a, b, sa, sb, 1, r0, c0, lane, vb, f0);
+      load_quarter<NT, GRID>(f1, a, b, sa, sb, 1, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 0, NT>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
-      load_quarter(f0, a, b, sa, sb, 2, r0, c0, lane, vb, f1);
+      load_quarter<NT, GRID>(f0, a, b, sa, sb, 2, r0, c0, lane, vb, f1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 2, NT>(f1, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
-      load_quarter(f1, a, b, sa, sb, 3, r0, c0, lane, vb, f0);
+      load_quarter<NT, GRID>(f1, a, b, sa, sb, 3, r0, c0, lane, vb, f0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 0, NT>(f0, acc, shift);
       __builtin_amdgcn_sched_barrier(0);
@@ -720,7 +747,7 @@ gemm_full_kernel(const GemmSet<NP> s, int rounds) {
         if (kt + 2 < nk) issue(pi, bm, bn, kt + 2, st);
         else if (rn < w.rounds && kt + 2 - nk < nk) issue(npi, nbm, nbn, kt + 2 - nk, st);
         st ^= 1;
-        load_quarter(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0), f1);
+        load_quarter<NT, GRID>(f0, sA[st], sB[st], sSA[st], sSB[st], 0, r0, c0, lane, blocks_in(kt + 1 < nk ? kt + 1 : 0), f1);
       }
       __builtin_amdgcn_sched_barrier(0);
       mfma_quarter<GRID, 2, NT>(f1, acc, shift);
