@@ -30,7 +30,8 @@ and hot, RTNE and SR, the rotation ablation and the diagnostics kernel), the
 fused-QKV Fprop GEMM and the MLP Dgrad and Wgrad GEMMs on their own; `mxnorm` times the fused MXNorm + row-wise cast launch,
 `nvfp4` the double-block quantizer; `mfma_ceiling` the FP4 MFMA's rate on
 register-resident zero, constant and random operands; `roofline` is the dominant kernel's;
-`cpu_baseline` is the CPU oracle on bounded samples.
+`cpu_baseline` is the CPU oracle on bounded samples; `graph` is the same step
+recorded once as a HIP graph and replayed.
 """
 import argparse
 import json
@@ -255,6 +256,24 @@ def time_step(step, steps, stream):
         f["bytes"] += L.bytes
         f["flops"] += L.flops
     return ms_per_step, fam
+
+
+def time_graph(step, steps, stream):
+    """The same step recorded once as a HIP graph and replayed `steps` times between two events (no event
+    between its kernels, so no per-family split): the step's time with no host work per launch."""
+    import torch
+    g = step.capture()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": round(ms, 4), "value": round(step.flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+            "replays": steps}
 
 
 def gemm_peak(grid):
@@ -634,6 +653,8 @@ def main():
     if args.step_only:
         print(json.dumps({"ms_per_step": round(ms_per_step, 4), "kernels": kernels, "roofline": roof}), flush=True)
         return 0
+    graph = time_graph(step, args.steps, stream)
+    log("graph replay: %.3f ms/step" % graph["ms_per_step"])
     mxnorm = measure_mxnorm(tensors, dev)
     block16 = measure_block16(tensors, dev)
     # the same step on the other grid (the uniform E1M2 grid's GEMMs run on the FP8 matrix path)
@@ -685,6 +706,7 @@ def main():
         "gemm": {"TFLOP/s": round(gemm_tf, 1), "frac_mfma": round(gemm_tf / peak, 4),
                  "ms_per_step": round(gms, 4)},
         "kernels": kernels,
+        "graph": graph,
         "step_" + other: other_step,
         "workloads": configs,
         "mxnorm": mxnorm,

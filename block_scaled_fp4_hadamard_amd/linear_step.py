@@ -171,6 +171,20 @@ class LlamaBlockStep:
         for L in self.launches:
             L.fn()
 
+    def capture(self):
+        """One step recorded as a HIP graph (torch.cuda.CUDAGraph): the same launches on the same
+        preallocated operands and outputs; replay() reruns them with no host work per kernel.  Nothing in
+        a step allocates, synchronizes or clears memory, so the recorded step is the eager one."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()                        # warm-up on the capture stream's side, as torch asks
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            self.run()
+        return g
+
     @property
     def gemms(self):
         return sum(L.gemms for L in self.launches)
