@@ -40,7 +40,10 @@ __device__ __forceinline__ uint32_t cast_one(float yy, uint32_t byte, uint32_t u
     const int ebias = (int)byte - 127;
     uint32_t k;
     if constexpr (ROUND == MX_ROUND_RTNE) {
-      k = (uint32_t)rintf(ldexpf(fabsf(yy), 2 - ebias));
+      // t + 2^23 rounds t (< 2^23) to the nearest integer, ties to even, into the mantissa's low bits; the
+      // bit pattern's unsigned min with that of 2^23 + 7 then saturates as min(k, 7) does
+      const float f = ldexpf(fabsf(yy), 2 - ebias) + 8388608.0f;
+      return (min(__float_as_uint(f), 0x4B000007u) & 7u) | ((__float_as_uint(yy) >> 28) & 8u);
     } else {
       // u holds the 16-bit draw r in its top half.  T = floor(t * 2^16) (exact scaling, truncating
       // conversion) is floor(t) * 2^16 + floor(f * 2^16), so floor(t) rounds up iff floor(f * 2^16) + r >= 2^16,
