@@ -80,3 +80,20 @@ def test_stats_on_a_strided_unaligned_view(had_n):
     assert got["blocks"] == blocks and got["hist"] == hist.tolist()
     assert got["sum_sq"] == pytest.approx(s2, rel=1e-9)
     assert got["sum_err_sq"] == pytest.approx(e2, rel=1e-9)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_stats_full_size(axis):
+    """The size the benchmark times: the quantizer workload's 8192 x 4096 activation, H32 deterministic, its
+    E2M1 RTNE output on each axis; the totals over all 1,048,576 blocks against the oracle's."""
+    announce("quant stats full size %s 8192x4096 H32" % axis)
+    bits = synth.quant_x()
+    x = to_gpu_bits(bits)
+    q = quantize(x, axis=axis, had_n=32, had_kind="det")[axis]
+    got = quant_stats(x, q, axis, "e2m1", 32, "det", 0)
+    torch.cuda.synchronize()
+    codes, scales = qt_to_np(q)
+    s2, e2, hist, blocks = quant_stats_ref(bits, codes, scales, axis, "e2m1", 32, "det", 0)
+    assert got["blocks"] == blocks == 1048576 and got["hist"] == hist.tolist()
+    assert got["sum_sq"] == pytest.approx(s2, rel=1e-9)
+    assert got["sum_err_sq"] == pytest.approx(e2, rel=1e-9)
